@@ -1,0 +1,153 @@
+"""Python binding of libfgfp8.so: fine-grained block-scaled FP8 cast and NT GEMM on MI355X.
+
+Argument marshalling only.  Each function takes PyTorch tensors that already
+live on the GPU, passes their pointers, sizes and strides to the C entry point
+of the same name (``include/fgfp8.h``) on the current stream, and raises on a
+non-zero return code.  Every step of the computation runs in the library's
+HIP kernels; there is no fallback: if the library is missing, ``load()``
+raises.
+
+Scale layouts follow the C ABI: a scale tensor of logical shape
+``[rows, groups]`` may be row-major or MN-major (``stride(0) == 1``), as
+``mn_major_scales`` allocates it for the GEMM's LHS.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+IN_BF16, IN_FP32 = 0, 1
+SF_FP32, SF_UE8M0, SF_PACKED_UE8M0 = 0, 1, 2
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfgfp8.so")
+_lib = None
+
+
+class Fgfp8Error(RuntimeError):
+    pass
+
+
+def load():
+    """Load libfgfp8.so (built in-tree by ``_build.build()``); raise if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise Fgfp8Error(f"{LIB_PATH} is not built; run __graft_entry__.build()")
+    lib = ctypes.CDLL(LIB_PATH)
+    p, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.cast_per_token.argtypes = [p, i32, i64, i64, i64, i64, i32, i32, p, i64, p, i64, i64, p]
+    lib.cast_per_block.argtypes = [p, i32, i64, i64, i64, i32, p, i64, p, i64, p, i64, p, i64, p]
+    lib.gemm_fp8_nt_bf16.argtypes = [p, i64, p, i32, i64, p, i64, p, i64, p, i64, i64, i64, i64, p]
+    lib.wgrad_gemm_fp8_nt_fp32.argtypes = [p, i64, p, i64, p, i64, p, i64, p, i64, i64, i64, i64, p]
+    for f in ("cast_per_token", "cast_per_block", "gemm_fp8_nt_bf16", "wgrad_gemm_fp8_nt_fp32"):
+        getattr(lib, f).restype = i32
+    lib.fgfp8_status_string.argtypes = [i32]
+    lib.fgfp8_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+EXPORTED = ("cast_per_token", "cast_per_block", "gemm_fp8_nt_bf16", "wgrad_gemm_fp8_nt_fp32",
+            "fgfp8_status_string")
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        msg = load().fgfp8_status_string(rc).decode()
+        raise Fgfp8Error(f"{what}: {msg} (status {rc})")
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _x_dtype(x: torch.Tensor) -> int:
+    if x.dtype == torch.bfloat16:
+        return IN_BF16
+    if x.dtype == torch.float32:
+        return IN_FP32
+    raise TypeError("input must be bfloat16 or float32")
+
+
+def _u8(t: torch.Tensor) -> torch.Tensor:
+    return t.view(torch.uint8) if t.dtype == torch.float8_e4m3fn else t
+
+
+# ---------------------------------------------------------------------------
+# allocation helpers (device memory only; no computation)
+# ---------------------------------------------------------------------------
+
+def mn_major_scales(rows: int, groups: int, dtype=torch.float32, device="cuda", align: int = 4):
+    """[rows, groups] tensor in MN-major layout: element (r, g) at g*ld + r, ld = align(rows, 4)."""
+    ld = -(-rows // align) * align
+    return torch.empty(groups, ld, dtype=dtype, device=device).t()[:rows]
+
+
+def num_groups(cols: int, gran_k: int) -> int:
+    return -(-cols // gran_k)
+
+
+# ---------------------------------------------------------------------------
+# entry points
+# ---------------------------------------------------------------------------
+
+def cast_per_token(x: torch.Tensor, q: torch.Tensor, sf: torch.Tensor, gran_k: int = 128,
+                   sf_fmt: int = SF_FP32) -> None:
+    """Per-token FP8 cast of a 2-D view ``x`` [rows, cols] (row-major or transposed) into
+    ``q`` (uint8 or float8_e4m3fn view [rows, cols]) and ``sf`` ([rows, G] float32, or
+    [rows, ceil(G/4)] int32 for packed UE8M0; row-major or MN-major view)."""
+    q = _u8(q)
+    rows, cols = x.shape
+    _check(load().cast_per_token(_ptr(x), _x_dtype(x), rows, cols, x.stride(0), x.stride(1), gran_k, sf_fmt,
+                                 _ptr(q), q.stride(0), _ptr(sf), sf.stride(0), sf.stride(1), _stream(x)),
+           "cast_per_token")
+
+
+def cast_per_block(x: torch.Tensor, q: torch.Tensor, sf: torch.Tensor, qT: torch.Tensor | None = None,
+                   sfT: torch.Tensor | None = None, sf_fmt: int = SF_FP32) -> None:
+    """128x128 block FP8 cast of row-major ``x`` [rows, cols] into ``q`` and ``sf``
+    [ceil(rows/128), ceil(cols/128)]; optionally also ``qT`` = q^T and ``sfT`` = sf^T."""
+    q = _u8(q)
+    qT = None if qT is None else _u8(qT)
+    rows, cols = x.shape
+    _check(load().cast_per_block(_ptr(x), _x_dtype(x), rows, cols, x.stride(0), sf_fmt, _ptr(q), q.stride(0),
+                                 _ptr(sf), sf.stride(0), _ptr(qT), 0 if qT is None else qT.stride(0),
+                                 _ptr(sfT), 0 if sfT is None else sfT.stride(0), _stream(x)),
+           "cast_per_block")
+
+
+def gemm_fp8_nt_bf16(A: torch.Tensor, sa: torch.Tensor, B: torch.Tensor, sb: torch.Tensor, D: torch.Tensor,
+                     sa_fmt: int = SF_FP32) -> None:
+    """D[m, n] (bf16) = (A*sa)(B*sb)^T.  sa: MN-major view [m, k/128] (float32) or
+    [m, ceil(k/512)] (int32, packed UE8M0); sb: [ceil(n/128), k/128] float32."""
+    A, B = _u8(A), _u8(B)
+    m, k = A.shape
+    n = B.shape[0]
+    if sa.shape[0] > 1 and sa.stride(0) != 1:
+        raise ValueError("sa must be MN-major (stride(0) == 1)")
+    sa_ld = sa.stride(1) if sa.dim() == 2 else m
+    _check(load().gemm_fp8_nt_bf16(_ptr(A), A.stride(0), _ptr(sa), sa_fmt, sa_ld, _ptr(B), B.stride(0),
+                                   _ptr(sb), sb.stride(0), _ptr(D), D.stride(0), m, n, k, _stream(A)),
+           "gemm_fp8_nt_bf16")
+
+
+def wgrad_gemm_fp8_nt_fp32(A: torch.Tensor, sa: torch.Tensor, B: torch.Tensor, sb: torch.Tensor,
+                           D: torch.Tensor) -> None:
+    """D[m, n] (float32) += (A*sa)(B*sb)^T with MN-major views sa [m, k/128], sb [n, k/128]."""
+    A, B = _u8(A), _u8(B)
+    m, k = A.shape
+    n = B.shape[0]
+    for s in (sa, sb):
+        if s.shape[0] > 1 and s.stride(0) != 1:
+            raise ValueError("wgrad scales must be MN-major (stride(0) == 1)")
+    _check(load().wgrad_gemm_fp8_nt_fp32(_ptr(A), A.stride(0), _ptr(sa), sa.stride(1), _ptr(B), B.stride(0),
+                                         _ptr(sb), sb.stride(1), _ptr(D), D.stride(0), m, n, k, _stream(A)),
+           "wgrad_gemm_fp8_nt_fp32")

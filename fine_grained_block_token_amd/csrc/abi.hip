@@ -1,0 +1,153 @@
+// abi.hip -- the extern "C" entry points of libfgfp8.so (declared in
+// include/fgfp8.h): host-side argument validation, the gfx950 device check,
+// and the launch on the caller's stream.  Every check runs before any HIP
+// call that could launch work, so an invalid call writes nothing.
+#include <atomic>
+#include <cstring>
+
+#include "fgfp8.h"
+#include "launch.h"
+
+namespace {
+
+using fgfp8::kInBf16;
+using fgfp8::kInFp32;
+using fgfp8::kSfFp32;
+using fgfp8::kSfPackedUe8m0;
+using fgfp8::kSfUe8m0;
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// 0 = not yet checked, 1 = gfx950, -1 = something else
+std::atomic<int> g_device_state[64];
+
+int check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return FGFP8_EDEVICE;
+  if (dev >= 64) return FGFP8_EDEVICE;
+  int s = g_device_state[dev].load(std::memory_order_relaxed);
+  if (s == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return FGFP8_EDEVICE;
+    s = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+    g_device_state[dev].store(s, std::memory_order_relaxed);
+  }
+  return s == 1 ? FGFP8_OK : FGFP8_EDEVICE;
+}
+
+int launched(hipError_t e) { return e == hipSuccess ? FGFP8_OK : FGFP8_ELAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+int cast_per_token(const void *x, int x_dtype, int64_t rows, int64_t cols, int64_t x_stride_row,
+                   int64_t x_stride_col, int gran_k, int sf_fmt, uint8_t *q, int64_t q_ld, void *sf,
+                   int64_t sf_stride_row, int64_t sf_stride_group, void *stream) {
+  if (x_dtype != kInBf16 && x_dtype != kInFp32) return FGFP8_EINVAL;
+  if (gran_k != 32 && gran_k != 128) return FGFP8_EINVAL;
+  if (sf_fmt != kSfFp32 && sf_fmt != kSfUe8m0 && sf_fmt != kSfPackedUe8m0) return FGFP8_EINVAL;
+  if (rows < 0 || cols < 0) return FGFP8_EINVAL;
+  if (rows == 0 || cols == 0) return FGFP8_OK;
+  if (!x || !q || !sf) return FGFP8_EINVAL;
+  const int64_t es = x_dtype == kInBf16 ? 2 : 4;
+  bool transposed;
+  if (x_stride_col == 1 && x_stride_row >= cols) {
+    transposed = false;
+    if ((x_stride_row * es) % 16 != 0 && rows > 1) return FGFP8_EINVAL;
+  } else if (x_stride_row == 1 && x_stride_col >= rows) {
+    transposed = true;
+    if ((x_stride_col * es) % 16 != 0) return FGFP8_EINVAL;
+  } else {
+    return FGFP8_EINVAL;
+  }
+  if (!aligned(x, 16)) return FGFP8_EINVAL;
+  const int64_t qa = transposed ? 16 : 8;
+  if (!aligned(q, qa) || q_ld < cols || q_ld % qa != 0) return FGFP8_EINVAL;
+  if (!aligned(sf, 4)) return FGFP8_EINVAL;
+  const int64_t groups = cdiv(cols, gran_k);
+  const int64_t units = sf_fmt == kSfPackedUe8m0 ? cdiv(groups, 4) : groups;
+  const bool row_major_sf = sf_stride_group == 1 && sf_stride_row >= units;
+  const bool mn_major_sf = sf_stride_row == 1 && sf_stride_group >= rows;
+  if (!row_major_sf && !mn_major_sf) return FGFP8_EINVAL;
+  const int dev = check_device();
+  if (dev != FGFP8_OK) return dev;
+  fgfp8::CastTokenArgs a{x, x_dtype, rows, cols, x_stride_row, x_stride_col, gran_k, sf_fmt,
+                         q, q_ld, sf, sf_stride_row, sf_stride_group};
+  return launched(fgfp8::launch_cast_per_token(a, static_cast<hipStream_t>(stream)));
+}
+
+int cast_per_block(const void *x, int x_dtype, int64_t rows, int64_t cols, int64_t x_ld, int sf_fmt,
+                   uint8_t *q, int64_t q_ld, float *sf, int64_t sf_ld, uint8_t *qT, int64_t qT_ld,
+                   float *sfT, int64_t sfT_ld, void *stream) {
+  if (x_dtype != kInBf16 && x_dtype != kInFp32) return FGFP8_EINVAL;
+  if (sf_fmt != kSfFp32 && sf_fmt != kSfUe8m0) return FGFP8_EINVAL;
+  if (rows < 0 || cols < 0) return FGFP8_EINVAL;
+  if ((qT == nullptr) != (sfT == nullptr)) return FGFP8_EINVAL;
+  if (rows == 0 || cols == 0) return FGFP8_OK;
+  if (!x || !q || !sf) return FGFP8_EINVAL;
+  const int64_t es = x_dtype == kInBf16 ? 2 : 4;
+  if (!aligned(x, 16) || x_ld < cols || (x_ld * es) % 16 != 0) return FGFP8_EINVAL;
+  if (!aligned(q, 8) || q_ld < cols || q_ld % 8 != 0) return FGFP8_EINVAL;
+  if (!aligned(sf, 4) || sf_ld < cdiv(cols, 128)) return FGFP8_EINVAL;
+  if (qT) {
+    if (!aligned(qT, 16) || qT_ld < rows || qT_ld % 16 != 0) return FGFP8_EINVAL;
+    if (!aligned(sfT, 4) || sfT_ld < cdiv(rows, 128)) return FGFP8_EINVAL;
+  }
+  const int dev = check_device();
+  if (dev != FGFP8_OK) return dev;
+  fgfp8::CastBlockArgs a{x, x_dtype, rows, cols, x_ld, sf_fmt, q, q_ld, sf, sf_ld, qT, qT_ld, sfT, sfT_ld};
+  return launched(fgfp8::launch_cast_per_block(a, static_cast<hipStream_t>(stream)));
+}
+
+static int check_gemm_common(const uint8_t *A, int64_t lda, const void *sa, int64_t sa_ld, const uint8_t *B,
+                             int64_t ldb, const float *sb, const void *D, int64_t m, int64_t n, int64_t k) {
+  if (m < 0 || n < 0 || k <= 0 || k % 128 != 0) return FGFP8_EINVAL;
+  if (m == 0 || n == 0) return FGFP8_OK;
+  if (!A || !B || !sa || !sb || !D) return FGFP8_EINVAL;
+  if (!aligned(A, 16) || lda < k || lda % 16 != 0) return FGFP8_EINVAL;
+  if (!aligned(B, 16) || ldb < k || ldb % 16 != 0) return FGFP8_EINVAL;
+  if (!aligned(sa, 4) || !aligned(sb, 4) || sa_ld < m) return FGFP8_EINVAL;
+  if (cdiv(m, 128) > 0x7FFFFFFF || cdiv(n, 128) > 0x7FFFFFFF) return FGFP8_EINVAL;
+  return 1;  // proceed
+}
+
+int gemm_fp8_nt_bf16(const uint8_t *A, int64_t lda, const void *sa, int sa_fmt, int64_t sa_ld,
+                     const uint8_t *B, int64_t ldb, const float *sb, int64_t sb_ld, uint16_t *D, int64_t ldd,
+                     int64_t m, int64_t n, int64_t k, void *stream) {
+  if (sa_fmt != kSfFp32 && sa_fmt != kSfUe8m0 && sa_fmt != kSfPackedUe8m0) return FGFP8_EINVAL;
+  const int c = check_gemm_common(A, lda, sa, sa_ld, B, ldb, sb, D, m, n, k);
+  if (c != 1) return c;
+  if (sb_ld < k / 128) return FGFP8_EINVAL;
+  if (!aligned(D, 16) || ldd < n || ldd % 8 != 0) return FGFP8_EINVAL;
+  const int dev = check_device();
+  if (dev != FGFP8_OK) return dev;
+  fgfp8::GemmArgs a{A, lda, sa, sa_fmt, sa_ld, B, ldb, sb, sb_ld, D, ldd, m, n, k, false};
+  return launched(fgfp8::launch_gemm(a, static_cast<hipStream_t>(stream)));
+}
+
+int wgrad_gemm_fp8_nt_fp32(const uint8_t *A, int64_t lda, const float *sa, int64_t sa_ld, const uint8_t *B,
+                           int64_t ldb, const float *sb, int64_t sb_ld, float *D, int64_t ldd, int64_t m,
+                           int64_t n, int64_t k, void *stream) {
+  const int c = check_gemm_common(A, lda, sa, sa_ld, B, ldb, sb, D, m, n, k);
+  if (c != 1) return c;
+  if (sb_ld < n) return FGFP8_EINVAL;
+  if (!aligned(D, 16) || ldd < n || ldd % 4 != 0) return FGFP8_EINVAL;
+  const int dev = check_device();
+  if (dev != FGFP8_OK) return dev;
+  fgfp8::GemmArgs a{A, lda, sa, kSfFp32, sa_ld, B, ldb, sb, sb_ld, D, ldd, m, n, k, true};
+  return launched(fgfp8::launch_gemm(a, static_cast<hipStream_t>(stream)));
+}
+
+const char *fgfp8_status_string(int status) {
+  switch (status) {
+    case FGFP8_OK: return "ok";
+    case FGFP8_EINVAL: return "invalid argument (nothing launched)";
+    case FGFP8_EDEVICE: return "current device is not gfx950";
+    case FGFP8_ELAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

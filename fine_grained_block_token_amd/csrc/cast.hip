@@ -1,0 +1,444 @@
+// cast.hip -- per-token and per-block FP8 (E4M3) cast kernels for gfx950.
+//
+// The cast is defined in "DeepGEMM Essentials: High-Performance FP8 Matrix
+// Multiplication", Part 3 (per token: amax of each 1x128 group along a row,
+// clamped at 1e-4; scale amax/448; each element times 448/amax rounded to
+// E4M3) and Part 4 (the same over 128x128 blocks), with the group-32,
+// UE8M0 and packed-UE8M0 options of "deep-gemm: fused per-token FP8 cast in
+// Triton".  Each kernel is one pass over HBM: every input byte is read once,
+// every output byte written once.
+#include "device_common.h"
+#include "launch.h"
+
+#pragma clang fp contract(off)
+
+namespace fgfp8 {
+namespace {
+
+constexpr int kThreads = 256;
+
+template <typename T>
+__device__ __forceinline__ void load8(const T *p, bool full, int valid, float (&v)[8]);
+
+// 8 bf16 (16 bytes) -> fp32; partial chunks read element by element.
+template <>
+__device__ __forceinline__ void load8<uint16_t>(const uint16_t *p, bool full, int valid, float (&v)[8]) {
+  if (full) {
+    const uint4 w = *reinterpret_cast<const uint4 *>(p);
+    v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x); v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
+    v[4] = bf16_lo(w.z); v[5] = bf16_hi(w.z); v[6] = bf16_lo(w.w); v[7] = bf16_hi(w.w);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = e < valid ? __uint_as_float((uint32_t)p[e] << 16) : 0.0f;
+  }
+}
+
+// 8 fp32 (two 16-byte loads).
+template <>
+__device__ __forceinline__ void load8<float>(const float *p, bool full, int valid, float (&v)[8]) {
+  if (full) {
+    const float4 a = *reinterpret_cast<const float4 *>(p);
+    const float4 b = *reinterpret_cast<const float4 *>(p + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = e < valid ? p[e] : 0.0f;
+  }
+}
+
+__device__ __forceinline__ uint32_t abs_bits(float f) { return __float_as_uint(f) & 0x7FFFFFFFu; }
+
+// ---------------------------------------------------------------------------
+// Per-token cast, row-major input.
+//
+// A "task" is one wave-wide step over a row: 64 lanes x 8 elements = 512
+// consecutive columns, i.e. 4 groups of 128 (16 lanes each) or 16 groups of
+// 32 (4 lanes each).  Each wave walks a contiguous range of tasks (row-major
+// order), U tasks at a time so that U 16-byte loads per lane are in flight.
+// The group amax is reduced with DPP inside the 16-lane rows; packed UE8M0
+// words are assembled with a DPP OR (group 32) or four readlanes (group 128).
+// ---------------------------------------------------------------------------
+template <typename TIn, int GRAN, int FMT>
+__global__ __launch_bounds__(kThreads) void cast_tok_rows_kernel(
+    const TIn *__restrict__ x, int64_t cols, int64_t xs_row, uint8_t *__restrict__ q, int64_t q_ld,
+    void *__restrict__ sf, int64_t sf_s_row, int64_t sf_s_grp, int64_t steps_per_row, int64_t tasks,
+    int64_t tasks_per_wave) {
+  constexpr int L = GRAN / 8;  // lanes per group
+  constexpr int U = 4;
+  constexpr bool kUe8m0 = FMT != kSfFp32;
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = (int64_t)blockIdx.x * (kThreads / kWave) + (threadIdx.x >> 6);
+  const int64_t t_begin = wave * tasks_per_wave;
+  const int64_t t_end = min(t_begin + tasks_per_wave, tasks);
+
+  for (int64_t tb = t_begin; tb < t_end; tb += U) {
+    float v[U][8];
+    int64_t row[U], col[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t t = tb + u;
+      row[u] = 0;
+      col[u] = cols;  // marks the lane idle
+      if (t < t_end) {
+        const int64_t r = t / steps_per_row;
+        const int64_t s = t - r * steps_per_row;
+        row[u] = r;
+        col[u] = (s * kWave + lane) * 8;
+      }
+      const bool live = col[u] < cols;
+      const bool full = col[u] + 8 <= cols;
+      if (live) {
+        load8<TIn>(x + row[u] * xs_row + col[u], full, (int)(cols - col[u]), v[u]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[u][e] = 0.0f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (tb + u >= t_end) break;  // uniform across the wave
+      uint32_t am = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) am = max(am, abs_bits(v[u][e]));
+      am = group_max_u32<L>(am);
+      const GroupScale gs = group_scale<kUe8m0>(__uint_as_float(am));
+      const float mu = gs.mult;
+      const uint32_t w0 = e4m3x4(v[u][0] * mu, v[u][1] * mu, v[u][2] * mu, v[u][3] * mu);
+      const uint32_t w1 = e4m3x4(v[u][4] * mu, v[u][5] * mu, v[u][6] * mu, v[u][7] * mu);
+      const int64_t c = col[u];
+      uint8_t *qp = q + row[u] * q_ld + c;
+      if (c + 8 <= cols) {
+        *reinterpret_cast<uint2 *>(qp) = make_uint2(w0, w1);
+      } else if (c < cols) {
+        const int valid = (int)(cols - c);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (e < valid) qp[e] = (uint8_t)((e < 4 ? w0 >> (8 * e) : w1 >> (8 * (e - 4))) & 0xFFu);
+      }
+      const int64_t g = c / GRAN;  // group of this lane
+      if constexpr (FMT != kSfPackedUe8m0) {
+        if ((lane % L) == 0 && c < cols)
+          reinterpret_cast<float *>(sf)[row[u] * sf_s_row + g * sf_s_grp] = gs.sf;
+      } else {
+        const uint32_t mine = c < cols ? gs.e8 << (8 * (g & 3)) : 0u;
+        uint32_t word;
+        if constexpr (GRAN == 32) {
+          word = group_or_u32<16>(mine);
+        } else {
+          word = (uint32_t)__builtin_amdgcn_readlane((int)mine, 0) |
+                 (uint32_t)__builtin_amdgcn_readlane((int)mine, 16) |
+                 (uint32_t)__builtin_amdgcn_readlane((int)mine, 32) |
+                 (uint32_t)__builtin_amdgcn_readlane((int)mine, 48);
+        }
+        if ((lane % (4 * L)) == 0 && c < cols)
+          reinterpret_cast<uint32_t *>(sf)[row[u] * sf_s_row + (g >> 2) * sf_s_grp] = word;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Per-token cast of a transposed view (the wgrad operands: groups run along
+// the tokens, which are the rows of the underlying row-major matrix).
+//
+// One workgroup owns 64 features (rows of the view) x 128 tokens (columns of
+// the view).  Phase 1 reads the tile with coalesced 16-byte loads along the
+// features and writes it to LDS transposed (fp32); phase 2 lets each thread
+// own 32 consecutive tokens of one feature, so the group amax needs at most a
+// 4-lane DPP reduction and the E4M3 row is written with 16-byte stores.  The
+// LDS column index is XOR-swizzled so both phases are free of bank conflicts.
+// For packed UE8M0 with group 128 a word spans 512 tokens, so a workgroup
+// then walks 4 tiles along the tokens.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int tile_col(int f, int tok) {
+  const int s = (((tok >> 5) & 3) << 2) ^ (((f >> 3) & 3) << 3) ^ ((f & 1) << 4);
+  return f * 128 + (tok ^ s);
+}
+
+template <typename TIn, int GRAN, int FMT>
+__global__ __launch_bounds__(kThreads) void cast_tok_cols_kernel(
+    const TIn *__restrict__ x, int64_t rows, int64_t cols, int64_t ld, uint8_t *__restrict__ q,
+    int64_t q_ld, void *__restrict__ sf, int64_t sf_s_row, int64_t sf_s_grp) {
+  constexpr int NT = (FMT == kSfPackedUe8m0 && GRAN == 128) ? 4 : 1;
+  constexpr bool kUe8m0 = FMT != kSfFp32;
+  __shared__ __attribute__((aligned(16))) float tile[64 * 128];
+  const int t = threadIdx.x;
+  const int64_t f0 = (int64_t)blockIdx.x * 64;
+  const int64_t cbase = (int64_t)blockIdx.y * (128 * NT);
+  const int fl = t >> 2, p = t & 3;  // phase 2: feature, 32-token part
+  const int64_t f = f0 + fl;
+  uint32_t word128 = 0;
+
+  for (int it = 0; it < NT; ++it) {
+    const int64_t c0 = cbase + (int64_t)it * 128;
+    if (c0 >= cols) break;  // uniform
+    // ---- phase 1: global -> LDS (transposed) ----
+    if constexpr (sizeof(TIn) == 2) {
+      const int tr = t >> 3, fc = t & 7;
+      const int64_t fb = f0 + 8 * fc;
+      const bool fullf = fb + 8 <= rows;
+      const int validf = (int)max<int64_t>(0, min<int64_t>(8, rows - fb));
+      float v[4][8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t c = c0 + 32 * i + tr;
+        if (c < cols && validf > 0) {
+          load8<TIn>(x + c * ld + fb, fullf, validf, v[i]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[i][e] = 0.0f;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) tile[tile_col(8 * fc + e, 32 * i + tr)] = v[i][e];
+    } else {
+      const int tr = t >> 4, fc = t & 15;
+      const int64_t fb = f0 + 4 * fc;
+      const bool fullf = fb + 4 <= rows;
+      const int validf = (int)max<int64_t>(0, min<int64_t>(4, rows - fb));
+      float v[8][4];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int64_t c = c0 + 16 * i + tr;
+        if (c < cols && fullf) {
+          const float4 a = *reinterpret_cast<const float4 *>(x + c * ld + fb);
+          v[i][0] = a.x; v[i][1] = a.y; v[i][2] = a.z; v[i][3] = a.w;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[i][e] = (c < cols && e < validf) ? x[c * ld + fb + e] : 0.0f;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) tile[tile_col(4 * fc + e, 16 * i + tr)] = v[i][e];
+    }
+    __syncthreads();
+
+    // ---- phase 2: each thread owns tokens [32p, 32p+32) of feature fl ----
+    float v[32];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const float4 a = *reinterpret_cast<const float4 *>(&tile[tile_col(fl, 32 * p + 4 * m)]);
+      v[4 * m] = a.x; v[4 * m + 1] = a.y; v[4 * m + 2] = a.z; v[4 * m + 3] = a.w;
+    }
+    uint32_t am = 0;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) am = max(am, abs_bits(v[e]));
+    if constexpr (GRAN == 128) am = group_max_u32<4>(am);
+    const GroupScale gs = group_scale<kUe8m0>(__uint_as_float(am));
+    uint32_t w[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+      w[m] = e4m3x4(v[4 * m] * gs.mult, v[4 * m + 1] * gs.mult, v[4 * m + 2] * gs.mult,
+                    v[4 * m + 3] * gs.mult);
+    const int64_t cp = c0 + 32 * p;  // first token of this thread
+    if (f < rows && cp < cols) {
+      uint8_t *qp = q + f * q_ld + cp;
+      if (cp + 32 <= cols) {
+        reinterpret_cast<uint4 *>(qp)[0] = make_uint4(w[0], w[1], w[2], w[3]);
+        reinterpret_cast<uint4 *>(qp)[1] = make_uint4(w[4], w[5], w[6], w[7]);
+      } else {
+        const int valid = (int)(cols - cp);
+#pragma unroll
+        for (int e = 0; e < 32; ++e)
+          if (e < valid) qp[e] = (uint8_t)((w[e >> 2] >> (8 * (e & 3))) & 0xFFu);
+      }
+    }
+    if constexpr (FMT != kSfPackedUe8m0) {
+      float *sp = reinterpret_cast<float *>(sf);
+      if (f < rows) {
+        if constexpr (GRAN == 128) {
+          if (p == 0) sp[f * sf_s_row + (c0 / 128) * sf_s_grp] = gs.sf;
+        } else {
+          if (cp < cols) sp[f * sf_s_row + (cp / 32) * sf_s_grp] = gs.sf;
+        }
+      }
+    } else if constexpr (GRAN == 32) {
+      // the 4 groups of this tile form one word; part p is group 4w + p
+      const uint32_t mine = cp < cols ? gs.e8 << (8 * p) : 0u;
+      const uint32_t word = group_or_u32<4>(mine);
+      if (p == 0 && f < rows) reinterpret_cast<uint32_t *>(sf)[f * sf_s_row + (c0 / 128) * sf_s_grp] = word;
+    } else {
+      word128 |= gs.e8 << (8 * it);
+    }
+    __syncthreads();  // the next tile overwrites the LDS tile
+  }
+  if constexpr (FMT == kSfPackedUe8m0 && GRAN == 128) {
+    if (p == 0 && f < rows && cbase < cols)
+      reinterpret_cast<uint32_t *>(sf)[f * sf_s_row + (cbase / 512) * sf_s_grp] = word128;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Per-block cast: one workgroup per 128x128 block.  Each thread holds 8 rows
+// x 8 columns in registers; the block amax is a DPP + LDS reduction.  The
+// optional transposed output goes through a 128x128 byte tile in LDS.
+// ---------------------------------------------------------------------------
+constexpr int kTPitch = 132;  // bytes per row of the transpose tile
+
+template <typename TIn, bool UE8M0, bool TRANS>
+__global__ __launch_bounds__(kThreads) void cast_block_kernel(
+    const TIn *__restrict__ x, int64_t rows, int64_t cols, int64_t x_ld, uint8_t *__restrict__ q,
+    int64_t q_ld, float *__restrict__ sf, int64_t sf_ld, uint8_t *__restrict__ qT, int64_t qT_ld,
+    float *__restrict__ sfT, int64_t sfT_ld) {
+  __shared__ uint32_t red[kThreads / kWave];
+  __shared__ __attribute__((aligned(16))) uint8_t tt[TRANS ? 128 * kTPitch : 4];
+  const int t = threadIdx.x;
+  const int64_t bi = blockIdx.y, bj = blockIdx.x;
+  const int64_t r0 = bi * 128, c0 = bj * 128;
+  const int cc = t & 15, rr = t >> 4;
+  const int64_t c = c0 + 8 * cc;
+  const bool colfull = c + 8 <= cols;
+  const int colvalid = (int)max<int64_t>(0, min<int64_t>(8, cols - c));
+
+  float v[8][8];
+  uint32_t am = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int64_t r = r0 + rr + 16 * i;
+    if (r < rows && colvalid > 0) {
+      load8<TIn>(x + r * x_ld + c, colfull, colvalid, v[i]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[i][e] = 0.0f;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) am = max(am, abs_bits(v[i][e]));
+  }
+  am = wave_max_u32(am);
+  if ((t & 63) == 0) red[t >> 6] = am;
+  __syncthreads();
+  am = max(max(red[0], red[1]), max(red[2], red[3]));
+  const GroupScale gs = group_scale<UE8M0>(__uint_as_float(am));
+
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int64_t r = r0 + rr + 16 * i;
+    const uint32_t w0 = e4m3x4(v[i][0] * gs.mult, v[i][1] * gs.mult, v[i][2] * gs.mult, v[i][3] * gs.mult);
+    const uint32_t w1 = e4m3x4(v[i][4] * gs.mult, v[i][5] * gs.mult, v[i][6] * gs.mult, v[i][7] * gs.mult);
+    if (r < rows && colvalid > 0) {
+      uint8_t *qp = q + r * q_ld + c;
+      if (colfull) {
+        *reinterpret_cast<uint2 *>(qp) = make_uint2(w0, w1);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (e < colvalid) qp[e] = (uint8_t)((e < 4 ? w0 >> (8 * e) : w1 >> (8 * (e - 4))) & 0xFFu);
+      }
+    }
+    if constexpr (TRANS) {
+      uint32_t *tp = reinterpret_cast<uint32_t *>(&tt[(rr + 16 * i) * kTPitch + 8 * cc]);
+      tp[0] = w0;
+      tp[1] = w1;
+    }
+  }
+  if (t == 0) {
+    sf[bi * sf_ld + bj] = gs.sf;
+    if constexpr (TRANS) sfT[bj * sfT_ld + bi] = gs.sf;
+  }
+  if constexpr (TRANS) {
+    __syncthreads();
+    // thread: column ct of the block (a row of q^T), rows [64h, 64h+64)
+    const int ct = t >> 1, h = t & 1;
+    const int64_t rowT = c0 + ct;
+    if (rowT < cols) {
+      uint32_t w[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int rb = 64 * h + 4 * j;
+        w[j] = (uint32_t)tt[(rb + 0) * kTPitch + ct] | ((uint32_t)tt[(rb + 1) * kTPitch + ct] << 8) |
+               ((uint32_t)tt[(rb + 2) * kTPitch + ct] << 16) | ((uint32_t)tt[(rb + 3) * kTPitch + ct] << 24);
+      }
+      const int64_t rbase = r0 + 64 * h;
+      uint8_t *op = qT + rowT * qT_ld + rbase;
+      if (rbase + 64 <= rows) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          reinterpret_cast<uint4 *>(op)[j] = make_uint4(w[4 * j], w[4 * j + 1], w[4 * j + 2], w[4 * j + 3]);
+      } else if (rbase < rows) {
+        const int valid = (int)(rows - rbase);
+        for (int e = 0; e < valid; ++e) op[e] = (uint8_t)((w[e >> 2] >> (8 * (e & 3))) & 0xFFu);
+      }
+    }
+  }
+}
+
+template <typename TIn, int GRAN, int FMT>
+hipError_t launch_tok_rows(const void *x, int64_t rows, int64_t cols, int64_t xs_row, uint8_t *q,
+                           int64_t q_ld, void *sf, int64_t sf_s_row, int64_t sf_s_grp, hipStream_t st) {
+  const int64_t steps = (cols + 511) / 512;
+  const int64_t tasks = rows * steps;
+  const int64_t target_waves = 8192;  // ~8 workgroups of 4 waves per CU
+  int64_t tpw = (tasks + target_waves - 1) / target_waves;
+  if (tpw < 1) tpw = 1;
+  const int64_t waves = (tasks + tpw - 1) / tpw;
+  const int64_t blocks = (waves + 3) / 4;
+  hipLaunchKernelGGL((cast_tok_rows_kernel<TIn, GRAN, FMT>), dim3((unsigned)blocks), dim3(kThreads), 0, st,
+                     reinterpret_cast<const TIn *>(x), cols, xs_row, q, q_ld, sf, sf_s_row, sf_s_grp, steps,
+                     tasks, tpw);
+  return hipGetLastError();
+}
+
+template <typename TIn, int GRAN, int FMT>
+hipError_t launch_tok_cols(const void *x, int64_t rows, int64_t cols, int64_t ld, uint8_t *q, int64_t q_ld,
+                           void *sf, int64_t sf_s_row, int64_t sf_s_grp, hipStream_t st) {
+  constexpr int NT = (FMT == kSfPackedUe8m0 && GRAN == 128) ? 4 : 1;
+  const dim3 grid((unsigned)((rows + 63) / 64), (unsigned)((cols + 128 * NT - 1) / (128 * NT)));
+  hipLaunchKernelGGL((cast_tok_cols_kernel<TIn, GRAN, FMT>), grid, dim3(kThreads), 0, st,
+                     reinterpret_cast<const TIn *>(x), rows, cols, ld, q, q_ld, sf, sf_s_row, sf_s_grp);
+  return hipGetLastError();
+}
+
+template <typename TIn>
+hipError_t dispatch_tok(bool transposed, int gran, int fmt, const void *x, int64_t rows, int64_t cols,
+                        int64_t xs, uint8_t *q, int64_t q_ld, void *sf, int64_t s_row, int64_t s_grp,
+                        hipStream_t st) {
+#define FGFP8_TOK(G, F)                                                                          \
+  if (gran == G && fmt == F)                                                                     \
+    return transposed ? launch_tok_cols<TIn, G, F>(x, rows, cols, xs, q, q_ld, sf, s_row, s_grp, st) \
+                      : launch_tok_rows<TIn, G, F>(x, rows, cols, xs, q, q_ld, sf, s_row, s_grp, st);
+  FGFP8_TOK(128, kSfFp32)
+  FGFP8_TOK(128, kSfUe8m0)
+  FGFP8_TOK(128, kSfPackedUe8m0)
+  FGFP8_TOK(32, kSfFp32)
+  FGFP8_TOK(32, kSfUe8m0)
+  FGFP8_TOK(32, kSfPackedUe8m0)
+#undef FGFP8_TOK
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_cast_per_token(const CastTokenArgs &a, hipStream_t st) {
+  const bool transposed = a.x_stride_col != 1;
+  const int64_t xs = transposed ? a.x_stride_col : a.x_stride_row;
+  if (a.x_dtype == kInBf16)
+    return dispatch_tok<uint16_t>(transposed, a.gran_k, a.sf_fmt, a.x, a.rows, a.cols, xs, a.q, a.q_ld, a.sf,
+                                  a.sf_stride_row, a.sf_stride_group, st);
+  return dispatch_tok<float>(transposed, a.gran_k, a.sf_fmt, a.x, a.rows, a.cols, xs, a.q, a.q_ld, a.sf,
+                             a.sf_stride_row, a.sf_stride_group, st);
+}
+
+hipError_t launch_cast_per_block(const CastBlockArgs &a, hipStream_t st) {
+  const dim3 grid((unsigned)((a.cols + 127) / 128), (unsigned)((a.rows + 127) / 128));
+  const bool ue = a.sf_fmt == kSfUe8m0;
+  const bool tr = a.qT != nullptr;
+#define FGFP8_BLK(T, U, TR)                                                                              \
+  hipLaunchKernelGGL((cast_block_kernel<T, U, TR>), grid, dim3(kThreads), 0, st,                        \
+                     reinterpret_cast<const T *>(a.x), a.rows, a.cols, a.x_ld, a.q, a.q_ld, a.sf, a.sf_ld, \
+                     a.qT, a.qT_ld, a.sfT, a.sfT_ld)
+  if (a.x_dtype == kInBf16) {
+    if (ue) { if (tr) FGFP8_BLK(uint16_t, true, true); else FGFP8_BLK(uint16_t, true, false); }
+    else    { if (tr) FGFP8_BLK(uint16_t, false, true); else FGFP8_BLK(uint16_t, false, false); }
+  } else {
+    if (ue) { if (tr) FGFP8_BLK(float, true, true); else FGFP8_BLK(float, true, false); }
+    else    { if (tr) FGFP8_BLK(float, false, true); else FGFP8_BLK(float, false, false); }
+  }
+#undef FGFP8_BLK
+  return hipGetLastError();
+}
+
+}  // namespace fgfp8

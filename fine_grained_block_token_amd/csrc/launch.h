@@ -1,0 +1,62 @@
+// launch.h -- internal interface between the C ABI (abi.cpp) and the kernel
+// files of libfgfp8.  Arguments arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fgfp8 {
+
+enum : int { kInBf16 = 0, kInFp32 = 1 };
+enum : int { kSfFp32 = 0, kSfUe8m0 = 1, kSfPackedUe8m0 = 2 };
+
+struct CastTokenArgs {
+  const void *x;
+  int x_dtype;
+  int64_t rows, cols, x_stride_row, x_stride_col;
+  int gran_k, sf_fmt;
+  uint8_t *q;
+  int64_t q_ld;
+  void *sf;
+  int64_t sf_stride_row, sf_stride_group;
+};
+
+struct CastBlockArgs {
+  const void *x;
+  int x_dtype;
+  int64_t rows, cols, x_ld;
+  int sf_fmt;
+  uint8_t *q;
+  int64_t q_ld;
+  float *sf;
+  int64_t sf_ld;
+  uint8_t *qT;
+  int64_t qT_ld;
+  float *sfT;
+  int64_t sfT_ld;
+};
+
+// One GEMM problem.  wgrad == false: D bf16, sb one scale per 128x128 block
+// ((nb, kb) at sb[nb*sb_ld + kb]).  wgrad == true: D fp32 accumulated,
+// sb one scale per row and K block ((j, kb) at sb[kb*sb_ld + j]).
+struct GemmArgs {
+  const uint8_t *A;
+  int64_t lda;
+  const void *sa;
+  int sa_fmt;
+  int64_t sa_ld;
+  const uint8_t *B;
+  int64_t ldb;
+  const float *sb;
+  int64_t sb_ld;
+  void *D;
+  int64_t ldd;
+  int64_t m, n, k;
+  bool wgrad;
+};
+
+hipError_t launch_cast_per_token(const CastTokenArgs &a, hipStream_t st);
+hipError_t launch_cast_per_block(const CastBlockArgs &a, hipStream_t st);
+hipError_t launch_gemm(const GemmArgs &a, hipStream_t st);
+
+}  // namespace fgfp8

@@ -1,0 +1,176 @@
+/*
+ * fgfp8.h -- C ABI of libfgfp8.so: fine-grained block-scaled FP8 cast and
+ * NT GEMM for AMD Instinct MI355X (gfx950).
+ *
+ * Plain C: pointers, sizes and an opaque stream.  Every pointer named as a
+ * tensor below is DEVICE memory owned by the caller; the library allocates
+ * nothing and keeps no state beyond a per-device "is this gfx950" check.
+ * `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ * Every call is asynchronous and stream-ordered; none synchronises the host.
+ *
+ * Return codes (every entry point):
+ *   FGFP8_OK (0)        launched (or nothing to do: a zero-sized problem)
+ *   FGFP8_EINVAL (-1)   invalid argument, detected on the host before any
+ *                       launch: nothing was written
+ *   FGFP8_EDEVICE (-2)  the current device is not gfx950 (or no device)
+ *   FGFP8_ELAUNCH (-3)  the kernel launch failed (hipGetLastError)
+ * Nothing aborts, throws or prints.
+ *
+ * Formats.  E4M3 is the OCP FP8 "fn" format (bias 7, largest finite 448, no
+ * infinities), one byte per element.  bf16 is the upper half of an fp32.
+ * Scale formats:
+ *   FGFP8_SF_FP32          fp32 scale = amax / 448
+ *   FGFP8_SF_UE8M0         fp32 holding 2^e, the least power of two >= amax/448
+ *   FGFP8_SF_PACKED_UE8M0  int32 words; byte b of word w is e + 127 of group
+ *                          4w + b (little-endian); unused bytes of the last
+ *                          word are 0
+ *
+ * Sources (web pages, cited by title and section):
+ *   "DeepGEMM Essentials: High-Performance FP8 Matrix Multiplication"
+ *     (dev.to), Parts 1, 3-6, 12-13, 18;
+ *   "[Help] Starter script for nn.Linear for fwd,bwd" (DeepGEMM issue #102):
+ *     forward / dgrad / wgrad composition and the RHS scale-row layout;
+ *   "deep-gemm: fused per-token FP8 cast in Triton" (kernels-community PR
+ *     #1326): cast options, caller-given output views, no host sync.
+ */
+#ifndef FGFP8_H
+#define FGFP8_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FGFP8_OK 0
+#define FGFP8_EINVAL (-1)
+#define FGFP8_EDEVICE (-2)
+#define FGFP8_ELAUNCH (-3)
+
+#define FGFP8_IN_BF16 0
+#define FGFP8_IN_FP32 1
+
+#define FGFP8_SF_FP32 0
+#define FGFP8_SF_UE8M0 1
+#define FGFP8_SF_PACKED_UE8M0 2
+
+/*
+ * cast_per_token -- per-token (1 x gran_k group) FP8 cast.
+ * Defined by "DeepGEMM Essentials", Part 3 (amax per 1x128 group along a
+ * row, clamped at 1e-4; scale amax/448; elements times 448/amax rounded to
+ * E4M3), with the group 32 / UE8M0 / packed-UE8M0 options and bf16 or fp32
+ * input of "deep-gemm: fused per-token FP8 cast in Triton".
+ *
+ * x          input, x_dtype FGFP8_IN_BF16 or FGFP8_IN_FP32, logical shape
+ *            [rows, cols]; element (r, c) at x[r*x_stride_row + c*x_stride_col]
+ *            (strides in elements).  Two layouts are accepted:
+ *              row-major view:  x_stride_col == 1, x_stride_row >= cols;
+ *              transposed view: x_stride_row == 1, x_stride_col >= rows
+ *              (the transpose of a row-major [cols, x_stride_col] matrix,
+ *              as the wgrad operands are read).
+ *            x must be 16-byte aligned and the non-unit stride a multiple of
+ *            16 bytes.
+ * gran_k     group size along the columns: 32 or 128.  Groups per row
+ *            G = ceil(cols / gran_k); a partial last group takes its amax
+ *            over its valid columns only.
+ * sf_fmt     FGFP8_SF_FP32, FGFP8_SF_UE8M0 or FGFP8_SF_PACKED_UE8M0.
+ * q          E4M3 output [rows, cols], element (r, c) at q[r*q_ld + c];
+ *            q 8-byte aligned, q_ld >= cols and a multiple of 8 (row-major
+ *            input) or of 16 (transposed input).
+ * sf         scales.  fp32 / UE8M0: float (r, g) at
+ *            sf[r*sf_stride_row + g*sf_stride_group], g < G.  Packed: int32
+ *            word (r, w) at sf[r*sf_stride_row + w*sf_stride_group],
+ *            w < ceil(G/4).  Row-major scales: (G or ceil(G/4), 1); the
+ *            GEMM's MN-major layout: (1, ld) with ld >= rows.  Strides must
+ *            be positive and the (r, g) -> offset map one-to-one.
+ * Writes exactly the rows x cols bytes of q and the rows x G scales (or
+ * rows x ceil(G/4) words) and nothing else of either buffer.
+ * rows == 0 or cols == 0: returns FGFP8_OK and launches nothing.
+ */
+int cast_per_token(const void *x, int x_dtype, int64_t rows, int64_t cols,
+                   int64_t x_stride_row, int64_t x_stride_col,
+                   int gran_k, int sf_fmt,
+                   uint8_t *q, int64_t q_ld,
+                   void *sf, int64_t sf_stride_row, int64_t sf_stride_group,
+                   void *stream);
+
+/*
+ * cast_per_block -- 128 x 128 block FP8 cast (the RHS / weight operand).
+ * Defined by "DeepGEMM Essentials", Part 4 (amax per 128x128 block, same
+ * clamp, scale and rounding as the per-token cast).  The optional transposed
+ * output is the exact transpose of (q, sf): the block cast commutes with
+ * transposition, so it is the dgrad RHS (the transpose of the FP8 weight in
+ * the maintainer's pseudo-code of "[Help] Starter script for nn.Linear for
+ * fwd,bwd") with no second rounding.
+ *
+ * x       bf16 or fp32 [rows, cols] row-major, leading dimension x_ld >= cols
+ *         (elements); 16-byte aligned, x_ld a multiple of 16 bytes.
+ * sf_fmt  FGFP8_SF_FP32 or FGFP8_SF_UE8M0 (fp32 holding 2^e).
+ * q       E4M3 [rows, cols], ld q_ld >= cols, multiple of 16; q 16-B aligned.
+ * sf      fp32 [ceil(rows/128), ceil(cols/128)], block (bi, bj) at
+ *         sf[bi*sf_ld + bj], sf_ld >= ceil(cols/128).
+ * qT      NULL, or E4M3 [cols, rows] = q^T, ld qT_ld >= rows, multiple of 16.
+ * sfT     NULL iff qT is NULL; fp32 [ceil(cols/128), ceil(rows/128)] = sf^T,
+ *         ld sfT_ld >= ceil(rows/128).
+ */
+int cast_per_block(const void *x, int x_dtype, int64_t rows, int64_t cols, int64_t x_ld,
+                   int sf_fmt, uint8_t *q, int64_t q_ld, float *sf, int64_t sf_ld,
+                   uint8_t *qT, int64_t qT_ld, float *sfT, int64_t sfT_ld,
+                   void *stream);
+
+/*
+ * gemm_fp8_nt_bf16 -- D = (A * sa)(B * sb)^T, bf16 output (forward, dgrad).
+ * Defined by "DeepGEMM Essentials", Parts 1 and 6 (LHS x RHS^T, LHS with
+ * per-token 1x128 scales in the column-major layout of Part 5, RHS with
+ * 128x128 block scales) and the reply in "[Help] Starter script for
+ * nn.Linear for fwd,bwd" that the RHS scale row (1 x ceil(k/128)) of an
+ * n-block serves every K block.  Within each 128-wide K block the products
+ * are summed in fp32; each block's partial sum is multiplied by
+ * sa(i, kb) * sb(j/128, kb) and added to an fp32 accumulator; the result is
+ * rounded to bf16 (nearest, ties to even).
+ *
+ * A       E4M3 [m, k] row-major, lda >= k, multiple of 16; 16-B aligned.
+ * sa      per-token scales in MN-major layout: sa_fmt FGFP8_SF_FP32 or
+ *         FGFP8_SF_UE8M0: float (i, kb) at sa[kb*sa_ld + i];
+ *         FGFP8_SF_PACKED_UE8M0: int32 word (i, kb/4) at sa[(kb/4)*sa_ld + i],
+ *         exponent byte kb%4.  sa_ld >= m.
+ * B       E4M3 [n, k] row-major, ldb >= k, multiple of 16; 16-B aligned.
+ * sb      fp32 [ceil(n/128), k/128] row-major: (nb, kb) at sb[nb*sb_ld + kb],
+ *         sb_ld >= k/128.
+ * D       bf16 [m, n] row-major, ldd >= n, multiple of 8; 16-B aligned.
+ * k must be a positive multiple of 128; m, n >= 0 arbitrary.
+ */
+int gemm_fp8_nt_bf16(const uint8_t *A, int64_t lda, const void *sa, int sa_fmt, int64_t sa_ld,
+                     const uint8_t *B, int64_t ldb, const float *sb, int64_t sb_ld,
+                     uint16_t *D, int64_t ldd, int64_t m, int64_t n, int64_t k,
+                     void *stream);
+
+/*
+ * wgrad_gemm_fp8_nt_fp32 -- D += (A * sa)(B * sb)^T in fp32 (weight gradient).
+ * Defined by "DeepGEMM Essentials", Parts 12-13 (the weight gradient is
+ * accumulated into an existing fp32 tensor, expected = original + dY^T x)
+ * and the wgrad line of the pseudo-code in "[Help] Starter script for
+ * nn.Linear for fwd,bwd" (both operands transposed so that K runs over
+ * tokens).  Both operands carry one scale per row and 128-wide K block; each
+ * K block's fp32 partial sum is multiplied by sa(i, kb) * sb(j, kb).
+ *
+ * A   E4M3 [m, k] (m = output features, k = tokens), lda >= k, multiple of 16.
+ * sa  fp32 (i, kb) at sa[kb*sa_ld + i], sa_ld >= m.
+ * B   E4M3 [n, k] (n = input features), ldb >= k, multiple of 16.
+ * sb  fp32 (j, kb) at sb[kb*sb_ld + j], sb_ld >= n.
+ * D   fp32 [m, n] row-major, ldd >= n, multiple of 4; read and written.
+ * k must be a positive multiple of 128.
+ */
+int wgrad_gemm_fp8_nt_fp32(const uint8_t *A, int64_t lda, const float *sa, int64_t sa_ld,
+                           const uint8_t *B, int64_t ldb, const float *sb, int64_t sb_ld,
+                           float *D, int64_t ldd, int64_t m, int64_t n, int64_t k,
+                           void *stream);
+
+/* Human-readable text of a return code (static storage). */
+const char *fgfp8_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FGFP8_H */

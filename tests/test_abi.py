@@ -1,0 +1,119 @@
+"""The C ABI on the CPU: the library loads, exports every entry point that
+include/fgfp8.h declares, and rejects invalid arguments on the host before
+touching the GPU (status -1, nothing launched).  No compute call is made."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fgfp8.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import fine_grained_block_token_amd as fg
+    return fg.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_four_calls():
+    names = declared_functions()
+    for f in ("cast_per_token", "cast_per_block", "gemm_fp8_nt_bf16", "wgrad_gemm_fp8_nt_fp32",
+              "fgfp8_status_string"):
+        assert f in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for rc in (0, -1, -2, -3):
+        assert lib.fgfp8_status_string(rc)
+    assert b"invalid" in lib.fgfp8_status_string(-1)
+
+
+# fake but 16-byte aligned addresses: validation rejects before any access
+P = ctypes.c_void_p(0x10000)
+Q = ctypes.c_void_p(0x20000)
+S = ctypes.c_void_p(0x30000)
+
+
+def tok(lib, **kw):
+    a = dict(x=P, dt=0, rows=4, cols=256, srow=256, scol=1, gran=128, fmt=0, q=Q, qld=256, sf=S,
+             sfr=2, sfg=1, st=None)
+    a.update(kw)
+    return lib.cast_per_token(a["x"], a["dt"], a["rows"], a["cols"], a["srow"], a["scol"], a["gran"],
+                              a["fmt"], a["q"], a["qld"], a["sf"], a["sfr"], a["sfg"], a["st"])
+
+
+@pytest.mark.parametrize("kw", [
+    dict(gran=64), dict(fmt=3), dict(dt=2), dict(rows=-1),
+    dict(x=None), dict(q=None), dict(sf=None),
+    dict(srow=255), dict(scol=2), dict(srow=7, scol=3),
+    dict(x=ctypes.c_void_p(0x10008)), dict(q=ctypes.c_void_p(0x20004)), dict(qld=200), dict(qld=260),
+    dict(sfr=1, sfg=1), dict(sfr=1, sfg=3), dict(sf=ctypes.c_void_p(0x30002)),
+])
+def test_cast_per_token_rejects(lib, kw):
+    assert tok(lib, **kw) == -1
+
+
+def test_cast_per_token_zero_size_is_ok(lib):
+    assert tok(lib, rows=0) == 0 and tok(lib, cols=0) == 0
+
+
+def blk(lib, **kw):
+    a = dict(x=P, dt=0, rows=256, cols=256, xld=256, fmt=0, q=Q, qld=256, sf=S, sfld=2, qT=None,
+             qTld=0, sfT=None, sfTld=0, st=None)
+    a.update(kw)
+    return lib.cast_per_block(a["x"], a["dt"], a["rows"], a["cols"], a["xld"], a["fmt"], a["q"], a["qld"],
+                              a["sf"], a["sfld"], a["qT"], a["qTld"], a["sfT"], a["sfTld"], a["st"])
+
+
+@pytest.mark.parametrize("kw", [
+    dict(fmt=2), dict(xld=100), dict(qld=252), dict(sfld=1), dict(qT=Q, qTld=256),
+    dict(sfT=S, sfTld=2), dict(qT=Q, qTld=255, sfT=S, sfTld=2), dict(x=None),
+])
+def test_cast_per_block_rejects(lib, kw):
+    assert blk(lib, **kw) == -1
+
+
+def gemm(lib, **kw):
+    a = dict(A=P, lda=256, sa=S, fmt=0, sald=128, B=Q, ldb=256, sb=S, sbld=2, D=P, ldd=256, m=128,
+             n=256, k=256, st=None)
+    a.update(kw)
+    return lib.gemm_fp8_nt_bf16(a["A"], a["lda"], a["sa"], a["fmt"], a["sald"], a["B"], a["ldb"], a["sb"],
+                                a["sbld"], a["D"], a["ldd"], a["m"], a["n"], a["k"], a["st"])
+
+
+@pytest.mark.parametrize("kw", [
+    dict(k=200), dict(k=0), dict(lda=200), dict(ldb=250), dict(sald=100), dict(sbld=1), dict(ldd=100),
+    dict(ldd=252), dict(fmt=5), dict(A=None), dict(D=ctypes.c_void_p(0x10004)), dict(m=-1),
+])
+def test_gemm_rejects(lib, kw):
+    assert gemm(lib, **kw) == -1
+
+
+def test_gemm_zero_size_is_ok(lib):
+    assert gemm(lib, m=0) == 0 and gemm(lib, n=0) == 0
+
+
+def wgrad(lib, **kw):
+    a = dict(A=P, lda=256, sa=S, sald=128, B=Q, ldb=256, sb=S, sbld=256, D=P, ldd=256, m=128, n=256,
+             k=256, st=None)
+    a.update(kw)
+    return lib.wgrad_gemm_fp8_nt_fp32(a["A"], a["lda"], a["sa"], a["sald"], a["B"], a["ldb"], a["sb"],
+                                      a["sbld"], a["D"], a["ldd"], a["m"], a["n"], a["k"], a["st"])
+
+
+@pytest.mark.parametrize("kw", [dict(sbld=100), dict(k=100), dict(ldd=254), dict(sb=None)])
+def test_wgrad_rejects(lib, kw):
+    assert wgrad(lib, **kw) == -1
