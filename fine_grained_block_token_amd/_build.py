@@ -14,6 +14,8 @@ HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     # no packed-fp32 instructions anywhere in the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in VGPRs (the promotion reads them with VALU instructions)
+    "-mllvm", "--amdgpu-mfma-vgpr-form",
     "-Wno-unused-command-line-argument",
 ]
 

@@ -2,23 +2,33 @@
 //
 // D = (A * sa)(B * sb)^T, A [m, k] and B [n, k] E4M3 row-major ("DeepGEMM
 // Essentials: High-Performance FP8 Matrix Multiplication", Parts 1 and 6).
-// For every 128-wide K block the products are summed in fp32 by one
-// V_MFMA_SCALE_F32_16X16X128_F8F6F4 per 16x16 output tile (neutral hardware
-// scales), and that block's partial sum is promoted into an fp32 register
-// accumulator with the fine-grained scales: sa(i, kb) * sb(j/128, kb) for
-// the forward/dgrad GEMM (one RHS scale per 128x128 block, whose row of
-// ceil(k/128) values serves every K block -- the reply in "[Help] Starter
-// script for nn.Linear for fwd,bwd"), or sa(i, kb) * sb(j, kb) for wgrad
-// ("DeepGEMM Essentials", Parts 12-13: fp32 output, accumulated in place).
+// For every 128-wide K block one V_MFMA_SCALE_F32_16X16X128_F8F6F4 (neutral
+// hardware scales) per 16x16 output tile produces that block's partial sum,
+// which is then promoted into an fp32 register accumulator with the
+// fine-grained scales: sa(i, kb) * sb(j/128, kb) for forward/dgrad (one RHS
+// scale per 128x128 block, whose row of ceil(k/128) values serves every K
+// block -- the reply in "[Help] Starter script for nn.Linear for fwd,bwd"),
+// or sa(i, kb) * sb(j, kb) for wgrad ("DeepGEMM Essentials", Parts 12-13:
+// fp32 output, accumulated in place).
 //
-// Kernel structure: 256 threads = 4 waves in a 2x2 grid over a 128x128
-// output tile, each wave 64x64 (4x4 MFMA tiles).  A and B K-tiles (128x128
-// bytes each) are double-buffered in LDS with a 16-byte XOR swizzle so the
-// MFMA fragment reads (ds_read_b128) are free of bank conflicts; the next
-// K-tile's global loads are issued before the current tile's MFMAs.  The
-// MFMA is issued with B as its first operand so each lane ends up holding
-// four consecutive output columns of one row (8-byte bf16 stores, 16-byte
-// fp32 read-modify-writes).
+// gfx950 design notes (measured on MI355X):
+//  * The FP8 MFMA sustains ~4.6 PF, but dependent fp32 VALU work issued right
+//    after it serialises with it.  So the promotion of block kb-1's partial
+//    sums is software-pipelined under block kb's MFMAs: each MFMA writes a
+//    fresh partial P[t] that is consumed one K block later, and the issue
+//    order is shaped MFMA / VALU / MFMA / VALU with sched_group_barrier.
+//    (The MFMA results are kept in VGPRs: -mllvm --amdgpu-mfma-vgpr-form.)
+//  * A and B K-tiles (128 bytes of K per row) are copied global -> LDS by
+//    global_load_lds_dwordx4 (no VGPR staging), two stages deep.  Each lane
+//    fetches the 16-byte chunk that belongs at its fixed LDS slot under a
+//    16-byte XOR swizzle (chunk ^ (row/2)%8), so fragment reads (ds_read_b128)
+//    are free of bank conflicts.
+//  * 256 threads = 4 waves in a 2x2 grid over a 128x128 output tile, each
+//    wave 64x64 = 4x4 MFMA tiles; 2 workgroups per CU.
+//  * B is the MFMA's first operand, so a lane holds four consecutive output
+//    columns of one row (8-byte bf16 stores, 16-byte fp32 read-modify-write).
+//  * Workgroups are mapped XCD by XCD onto bands of 8 m-tiles so that the
+//    tiles resident on one XCD share A and B panels in its L2.
 #include "device_common.h"
 #include "launch.h"
 
@@ -30,15 +40,41 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kBM = 128, kBN = 128, kBK = 128;
-constexpr int kGemmThreads = 256;
+constexpr int kBK = 128;
+constexpr int kXcds = 8;
+constexpr int kGroupM = 8;
 
-// byte offset of 16-byte chunk `chunk` (0..7) of tile row `row`
-__device__ __forceinline__ int swz(int row, int chunk) { return row * kBK + ((chunk ^ (row & 7)) << 4); }
+// Tile configuration: WAVES_M x WAVES_N waves, each owning a 64x64 output block;
+// STAGES LDS stages of (BM + BN) x 128 bytes.
+template <int WAVES_M, int WAVES_N, int STAGES>
+struct Cfg {
+  static constexpr int kWaves = WAVES_M * WAVES_N;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kBM = 64 * WAVES_M, kBN = 64 * WAVES_N;
+  static constexpr int kABytes = kBM * kBK, kBBytes = kBN * kBK;
+  static constexpr int kSaOff = kABytes + kBBytes;          // BM fp32 (or packed word) row scales
+  static constexpr int kSbOff = kSaOff + 4 * kBM;           // forward: 64 copies of one fp32; wgrad: BN fp32
+  static constexpr int kSaLoads = kBM / 64;                 // 4-byte direct loads of 64 lanes
+  static constexpr int kSbLoads = kBN / 64;
+  static constexpr int kStageBytes = kSbOff + 4 * kBN;
+  static constexpr int kALoads = kABytes / 1024 / kWaves;   // 1 KB direct loads per wave per stage
+  static constexpr int kBLoads = kBBytes / 1024 / kWaves;
+  static_assert(kALoads * 1024 * kWaves == kABytes && kBLoads * 1024 * kWaves == kBBytes, "tile split");
+  static constexpr int kStages = STAGES;
+  static constexpr int WAVES_N_ = WAVES_N;
+};
+
+// Byte offset of 16-byte chunk `chunk` (0..7) of tile row `row`.  The gfx950 LDS
+// serves 256 bytes per clock, i.e. 16 lanes of a ds_read_b128 at once; the 16
+// lanes of a fragment read touch rows r..r+15 at one logical chunk, so the XOR
+// key (row/2)%8 together with the row parity (which selects the 128-byte half
+// of the 256-byte bank row) spreads them over all 16 bank groups.
+__device__ __forceinline__ int swz_key(int row) { return (row >> 1) & 7; }
+__device__ __forceinline__ int swz(int row, int chunk) { return row * kBK + ((chunk ^ swz_key(row)) << 4); }
 
 // MFMA operand: lane l holds row (l & 15) and K bytes [32*(l>>4), 32*(l>>4)+32).
-// A and B fragments use the same K mapping, so the product is exact whatever
-// order the instruction assigns to the 128 K positions.
+// A and B fragments use the same K mapping, so the product does not depend on
+// which order the instruction assigns to the 128 K positions.
 __device__ __forceinline__ v8i frag(const uint8_t *tile, int row, int lane) {
   const int c = (lane >> 4) << 1;
   const u32x4 lo = *reinterpret_cast<const u32x4 *>(tile + swz(row, c));
@@ -55,6 +91,20 @@ __device__ __forceinline__ v4f mfma_k128(v8i a, v8i b) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, 0, 0, 0, 127, 0, 127);
 }
 
+typedef const void __attribute__((address_space(1))) *gptr_t;
+typedef void __attribute__((address_space(3))) *lptr_t;
+
+// 64 lanes x 16 bytes global -> LDS; the LDS destination of lane l is dst + 16*l
+// (dst is wave-uniform and goes to M0).  Issued as inline assembly so that the
+// compiler's wait insertion does not treat every later LDS read as possibly
+// aliasing the copy in flight; the kernel orders these copies with explicit
+// s_waitcnt vmcnt + s_barrier.
+__device__ __forceinline__ void load_lds16(const uint8_t *src, uint8_t *dst_wave) {
+  const uint32_t lds = (uint32_t)(uintptr_t)(lptr_t)dst_wave;
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               ::"v"(src), "s"(lds) : "memory", "m0");
+}
+
 template <int SA_FMT>
 __device__ __forceinline__ float load_sa(const void *sa, int64_t sa_ld, int64_t i, int kb) {
   if constexpr (SA_FMT == kSfPackedUe8m0) {
@@ -65,107 +115,176 @@ __device__ __forceinline__ float load_sa(const void *sa, int64_t sa_ld, int64_t 
   }
 }
 
-template <int SA_FMT, bool WGRAD>
-__global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * (kBM + kBN) * kBK];
-  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
-  const int wm = (wv >> 1) * 64, wn = (wv & 1) * 64;
-  const int64_t m0 = (int64_t)blockIdx.y * kBM, n0 = (int64_t)blockIdx.x * kBN;
+// Scales of one K block as the promotion uses them.
+struct BlockScales {
+  float sa[4];      // per row-subtile (the lane's row)
+  float sb;         // forward/dgrad: uniform over the wave's 64 columns
+  v4f sbj[4];       // wgrad: per column-subtile, 4 consecutive columns
+};
+
+__device__ __forceinline__ void load_lds4(const void *src, uint8_t *dst_wave) {
+  const uint32_t lds = (uint32_t)(uintptr_t)(lptr_t)dst_wave;
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               ::"v"(src), "s"(lds) : "memory", "m0");
+}
+
+// acc += P * scale for MFMA tile (mi, ni)
+template <bool WGRAD>
+__device__ __forceinline__ void promote(v4f &acc, const v4f &p, const BlockScales &s, int mi, int ni) {
+  if constexpr (!WGRAD) {
+    const float c = s.sa[mi] * s.sb;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[r] = __builtin_fmaf(p[r], c, acc[r]);
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[r] = __builtin_fmaf(p[r], s.sa[mi] * s.sbj[ni][r], acc[r]);
+  }
+}
+
+template <class C, int SA_FMT, bool WGRAD>
+__global__ __launch_bounds__(C::kThreads, 2) void gemm_kernel(GemmArgs g, int tiles_m, int tiles_n) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::kStages * C::kStageBytes];
+  const int t = threadIdx.x, lane = t & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wm = (wv / C::WAVES_N_) * 64, wn = (wv % C::WAVES_N_) * 64;
+
+  // XCD-aware tile order: block b runs on XCD b % 8; each XCD takes a contiguous
+  // range of tile ids, walked in bands of kGroupM m-tiles.
+  const int tiles = tiles_m * tiles_n;
+  const int per_xcd = (tiles + kXcds - 1) / kXcds;
+  const int tid = (int)(blockIdx.x % kXcds) * per_xcd + (int)(blockIdx.x / kXcds);
+  if (tid >= tiles) return;
+  const int band = tid / (kGroupM * tiles_n);
+  const int band_m = min(kGroupM, tiles_m - band * kGroupM);
+  const int in_band = tid - band * kGroupM * tiles_n;
+  const int tm = band * kGroupM + in_band % band_m;
+  const int tn = in_band / band_m;
+  const int64_t m0 = (int64_t)tm * C::kBM, n0 = (int64_t)tn * C::kBN;
   const int64_t m = g.m, n = g.n;
   const int KB = (int)(g.k / kBK);
 
-  // global -> LDS copy: 4 16-byte chunks of A and of B per thread per K-tile
-  const uint8_t *ga[4], *gb[4];
-  int so[4];
+  // Direct-to-LDS copy of one stage (tiles and scales of one K block).  Each 1 KB
+  // wave instruction fills 64 consecutive 16-byte slots; slot s holds row s/8,
+  // physical chunk s%8, i.e. logical chunk (s%8) ^ swz_key(row).  Wave wv issues
+  // tile instructions wv, wv + kWaves, ...; the scale rows (4 bytes per lane) are
+  // spread over the first waves.
+  uint32_t a_off[C::kALoads], b_off[C::kBLoads];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int id = t + kGemmThreads * i, row = id >> 3, cc = id & 7;
-    ga[i] = g.A + min(m0 + row, m - 1) * g.lda + cc * 16;   // rows past the edge re-read the last row
-    gb[i] = g.B + min(n0 + row, n - 1) * g.ldb + cc * 16;   // (valid memory; their outputs are dropped)
-    so[i] = swz(row, cc);
-  }
-  u32x4 ra[4], rb[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    ra[i] = *reinterpret_cast<const u32x4 *>(ga[i]);
-    rb[i] = *reinterpret_cast<const u32x4 *>(gb[i]);
+  for (int i = 0; i < C::kALoads; ++i) {
+    const int s = 64 * (i * C::kWaves + wv) + lane, row = s >> 3, chunk = (s & 7) ^ swz_key(row);
+    a_off[i] = (uint32_t)(min(m0 + row, m - 1) * g.lda) + (uint32_t)(chunk * 16);
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    *reinterpret_cast<u32x4 *>(smem + so[i]) = ra[i];
-    *reinterpret_cast<u32x4 *>(smem + kBM * kBK + so[i]) = rb[i];
+  for (int i = 0; i < C::kBLoads; ++i) {
+    const int s = 64 * (i * C::kWaves + wv) + lane, row = s >> 3, chunk = (s & 7) ^ swz_key(row);
+    b_off[i] = (uint32_t)(min(n0 + row, n - 1) * g.ldb) + (uint32_t)(chunk * 16);
   }
-  __syncthreads();
-
-  int64_t arow[4];
+  static_assert(C::kSaLoads + C::kSbLoads <= C::kWaves, "one scale load per wave at most");
+  const bool sa_loader = wv < C::kSaLoads;
+  const bool sb_loader = wv >= C::kSaLoads && wv < C::kSaLoads + C::kSbLoads;
+  int64_t scale_row;   // row of sa (or column of sb) this lane copies
+  if (sa_loader) {
+    scale_row = min(m0 + 64 * wv + lane, m - 1);
+  } else {
+    scale_row = min(n0 + 64 * (wv - C::kSaLoads) + lane, n - 1);
+  }
+  auto issue = [&](int kb, uint8_t *st) {
+    const uint8_t *ga = g.A + (int64_t)kb * kBK;
+    const uint8_t *gb = g.B + (int64_t)kb * kBK;
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi) arow[mi] = min(m0 + wm + 16 * mi + (lane & 15), m - 1);
-  int64_t bcol[4][4];
+    for (int i = 0; i < C::kALoads; ++i) load_lds16(ga + a_off[i], st + 1024 * (i * C::kWaves + wv));
 #pragma unroll
-  for (int ni = 0; ni < 4; ++ni)
+    for (int i = 0; i < C::kBLoads; ++i) load_lds16(gb + b_off[i], st + C::kABytes + 1024 * (i * C::kWaves + wv));
+    if (sa_loader) {
+      const int64_t col = SA_FMT == kSfPackedUe8m0 ? (kb >> 2) : kb;
+      load_lds4(reinterpret_cast<const uint32_t *>(g.sa) + col * g.sa_ld + scale_row, st + C::kSaOff + 256 * wv);
+    } else if (sb_loader) {
+      const float *src = WGRAD ? g.sb + (int64_t)kb * g.sb_ld + scale_row
+                               : g.sb + (n0 >> 7) * g.sb_ld + kb;   // forward: the tile's one block scale
+      load_lds4(src, st + C::kSbOff + 256 * (wv - C::kSaLoads));
+    }
+  };
+  auto read_scales = [&](int kb, const uint8_t *st, BlockScales &s) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) bcol[ni][r] = min(n0 + wn + 16 * ni + 4 * (lane >> 4) + r, n - 1);
-
-  v4f acc[4][4];
-#pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
-
-  for (int kb = 0; kb < KB; ++kb) {
-    const int cur = kb & 1;
-    const uint8_t *As = smem + cur * (kBM + kBN) * kBK;
-    const uint8_t *Bs = As + kBM * kBK;
-    if (kb + 1 < KB) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        ra[i] = *reinterpret_cast<const u32x4 *>(ga[i] + (int64_t)(kb + 1) * kBK);
-        rb[i] = *reinterpret_cast<const u32x4 *>(gb[i] + (int64_t)(kb + 1) * kBK);
+    for (int mi = 0; mi < 4; ++mi) {
+      const float v = *reinterpret_cast<const float *>(st + C::kSaOff + 4 * (wm + 16 * mi + (lane & 15)));
+      if constexpr (SA_FMT == kSfPackedUe8m0) {
+        s.sa[mi] = __uint_as_float(((__float_as_uint(v) >> (8 * (kb & 3))) & 0xFFu) << 23);
+      } else {
+        s.sa[mi] = v;
       }
     }
-    float sav[4];
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi) sav[mi] = load_sa<SA_FMT>(g.sa, g.sa_ld, arow[mi], kb);
-    float sbv = 0.0f;
-    float sbj[4][4];
     if constexpr (!WGRAD) {
-      sbv = g.sb[(n0 >> 7) * g.sb_ld + kb];
+      s.sb = *reinterpret_cast<const float *>(st + C::kSbOff);
     } else {
 #pragma unroll
       for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sbj[ni][r] = g.sb[(int64_t)kb * g.sb_ld + bcol[ni][r]];
+        s.sbj[ni] = *reinterpret_cast<const v4f *>(st + C::kSbOff + 4 * (wn + 16 * ni + 4 * (lane >> 4)));
     }
+  };
+
+  BlockScales prev;   // scales of the K block whose partial sums are pending
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi) prev.sa[mi] = 0.0f;
+  prev.sb = 0.0f;
+#pragma unroll
+  for (int ni = 0; ni < 4; ++ni) prev.sbj[ni] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+
+  v4f acc[16], p[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    acc[i] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+    p[i] = acc[i];
+  }
+
+  // Pipeline (S = STAGES): step kb first waits until stage kb%S has landed (its
+  // own loads, then a bare s_barrier for everyone's), reads block kb's fragments
+  // and scales, issues the copy of block kb+S-1 into the stage read one step
+  // earlier, and runs block kb's MFMAs interleaved with the promotion of block
+  // kb-1.  The wait and the barrier sit at the top so that the fragment reads (and
+  // hence the MFMAs) cannot be scheduled above them; __syncthreads() is not used
+  // because its fence would also drain the prefetched stages.  Waves issue
+  // kLoads or kLoads + 1 loads per stage; waiting for at most kLoads outstanding
+  // loads (the one later stage, with three stages) guarantees the current stage
+  // has landed.
+  constexpr int kLoads = C::kALoads + C::kBLoads;
+  constexpr int S = C::kStages;
+  static_assert(S == 2 || S == 3, "two or three stages");
+#pragma unroll
+  for (int j = 0; j < S - 1; ++j)
+    if (j < KB) issue(j, smem + j * C::kStageBytes);
+
+  for (int kb = 0; kb < KB; ++kb) {
+    if (S == 3 && kb + 1 < KB) {
+      asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(kLoads) : "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    }
+    const uint8_t *st = smem + (kb % S) * C::kStageBytes;
+    // all LDS reads of this stage precede the copy into the next free stage
+    BlockScales cur;
+    read_scales(kb, st, cur);
     v8i af[4], bf[4];
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi) af[mi] = frag(As, wm + 16 * mi + (lane & 15), lane);
+    for (int mi = 0; mi < 4; ++mi) af[mi] = frag(st, wm + 16 * mi + (lane & 15), lane);
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni) bf[ni] = frag(Bs, wn + 16 * ni + (lane & 15), lane);
+    for (int ni = 0; ni < 4; ++ni) bf[ni] = frag(st + C::kABytes, wn + 16 * ni + (lane & 15), lane);
+    if (kb + S - 1 < KB) issue(kb + S - 1, smem + ((kb + S - 1) % S) * C::kStageBytes);
+    // promote block kb-1 (scales `prev`) while block kb's MFMAs run
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
-#pragma unroll
-      for (int ni = 0; ni < 4; ++ni) {
-        const v4f p = mfma_k128(bf[ni], af[mi]);   // p[r] = block sum of (row i, column j + r)
-        if constexpr (!WGRAD) {
-          const float c = sav[mi] * sbv;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[mi][ni][r] = __builtin_fmaf(p[r], c, acc[mi][ni][r]);
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[mi][ni][r] = __builtin_fmaf(p[r], sav[mi] * sbj[ni][r], acc[mi][ni][r]);
-        }
-      }
+    for (int i = 0; i < 16; ++i) {
+      promote<WGRAD>(acc[i], p[i], prev, i >> 2, i & 3);
+      p[i] = mfma_k128(bf[i & 3], af[i >> 2]);
     }
-    if (kb + 1 < KB) {
-      uint8_t *An = smem + (cur ^ 1) * (kBM + kBN) * kBK;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        *reinterpret_cast<u32x4 *>(An + so[i]) = ra[i];
-        *reinterpret_cast<u32x4 *>(An + kBM * kBK + so[i]) = rb[i];
-      }
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                 // 1 MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, WGRAD ? 8 : 4, 0);      // its share of VALU
     }
-    __syncthreads();
+    prev = cur;
   }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) promote<WGRAD>(acc[i], p[i], prev, i >> 2, i & 3);
 
   // epilogue: lane holds row i, columns j..j+3 of every 16x16 tile
 #pragma unroll
@@ -176,7 +295,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs g) {
     for (int ni = 0; ni < 4; ++ni) {
       const int64_t j = n0 + wn + 16 * ni + 4 * (lane >> 4);
       if (j >= n) continue;
-      const v4f a = acc[mi][ni];
+      const v4f a = acc[4 * mi + ni];
       if constexpr (!WGRAD) {
         uint16_t *dp = reinterpret_cast<uint16_t *>(g.D) + i * g.ldd + j;
         const uint32_t h0 = bf16_rne(a[0]) | (bf16_rne(a[1]) << 16);
@@ -205,16 +324,26 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs g) {
 
 }  // namespace
 
-hipError_t launch_gemm(const GemmArgs &a, hipStream_t st) {
-  const dim3 grid((unsigned)((a.n + kBN - 1) / kBN), (unsigned)((a.m + kBM - 1) / kBM));
+template <class C>
+hipError_t launch_cfg(const GemmArgs &a, hipStream_t st) {
+  const int tiles_m = (int)((a.m + C::kBM - 1) / C::kBM), tiles_n = (int)((a.n + C::kBN - 1) / C::kBN);
+  const int tiles = tiles_m * tiles_n;
+  const int per_xcd = (tiles + kXcds - 1) / kXcds;
+  const dim3 grid((unsigned)(per_xcd * kXcds));
   if (a.wgrad) {
-    hipLaunchKernelGGL((gemm_kernel<kSfFp32, true>), grid, dim3(kGemmThreads), 0, st, a);
+    hipLaunchKernelGGL((gemm_kernel<C, kSfFp32, true>), grid, dim3(C::kThreads), 0, st, a, tiles_m, tiles_n);
   } else if (a.sa_fmt == kSfPackedUe8m0) {
-    hipLaunchKernelGGL((gemm_kernel<kSfPackedUe8m0, false>), grid, dim3(kGemmThreads), 0, st, a);
+    hipLaunchKernelGGL((gemm_kernel<C, kSfPackedUe8m0, false>), grid, dim3(C::kThreads), 0, st, a, tiles_m, tiles_n);
   } else {
-    hipLaunchKernelGGL((gemm_kernel<kSfFp32, false>), grid, dim3(kGemmThreads), 0, st, a);
+    hipLaunchKernelGGL((gemm_kernel<C, kSfFp32, false>), grid, dim3(C::kThreads), 0, st, a, tiles_m, tiles_n);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_gemm(const GemmArgs &a, hipStream_t st) {
+  // 128x128 output tiles, 4 waves, 2 LDS stages (66 KB): two workgroups per CU, so
+  // one workgroup's barrier and copy latency is covered by the other's MFMAs.
+  return launch_cfg<Cfg<2, 2, 2>>(a, st);
 }
 
 }  // namespace fgfp8
