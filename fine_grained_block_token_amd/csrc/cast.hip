@@ -51,19 +51,56 @@ __device__ __forceinline__ uint32_t abs_bits(float f) { return __float_as_uint(f
 // ---------------------------------------------------------------------------
 // Per-token cast, row-major input.
 //
-// A "task" is one wave-wide step over a row: 64 lanes x 8 elements = 512
-// consecutive columns, i.e. 4 groups of 128 (16 lanes each) or 16 groups of
-// 32 (4 lanes each).  Each wave walks a contiguous range of tasks (row-major
-// order), U tasks at a time so that U 16-byte loads per lane are in flight.
-// The group amax is reduced with DPP inside the 16-lane rows; packed UE8M0
-// words are assembled with a DPP OR (group 32) or four readlanes (group 128).
+// A "task" is one wave-wide step over a row: 64 lanes x 16 elements = 1024
+// consecutive columns, i.e. 8 groups of 128 (8 lanes each) or 32 groups of 32
+// (2 lanes each).  Each wave walks a contiguous range of tasks (row-major
+// order), U tasks at a time so that 2*U (bf16) or 4*U (fp32) 16-byte loads per
+// lane are in flight; E4M3 bytes leave as one 16-byte store per lane.  The
+// group amax is reduced with DPP inside the 16-lane rows; packed UE8M0 words
+// are assembled with a DPP OR (group 32) or readlanes (group 128).
 // ---------------------------------------------------------------------------
-template <typename TIn, int GRAN, int FMT>
+constexpr int kTokEl = 16;              // elements per lane per task
+constexpr int kTokSpan = 64 * kTokEl;   // columns per task
+
+// 16 elements kept as raw words until they are processed (8 words of bf16
+// pairs, or 16 fp32 words), so that U tasks of loads stay in flight cheaply.
+template <typename T>
+struct Raw16 {
+  static constexpr int kWords = 8 * (int)sizeof(T) / 2;
+  uint32_t w[kWords];
+  __device__ __forceinline__ float get(int e) const {
+    if constexpr (sizeof(T) == 2) return (e & 1) ? bf16_hi(w[e >> 1]) : bf16_lo(w[e >> 1]);
+    else return __uint_as_float(w[e]);
+  }
+};
+
+template <typename T>
+__device__ __forceinline__ void load16(const T *p, bool full, int valid, Raw16<T> &r) {
+  if (full) {
+#pragma unroll
+    for (int i = 0; i < Raw16<T>::kWords / 4; ++i) {
+      const uint4 v = reinterpret_cast<const uint4 *>(p)[i];
+      r.w[4 * i] = v.x; r.w[4 * i + 1] = v.y; r.w[4 * i + 2] = v.z; r.w[4 * i + 3] = v.w;
+    }
+  } else if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t lo = 2 * i < valid ? (uint32_t)p[2 * i] : 0u;
+      const uint32_t hi = 2 * i + 1 < valid ? (uint32_t)p[2 * i + 1] : 0u;
+      r.w[i] = lo | (hi << 16);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) r.w[i] = i < valid ? __float_as_uint(p[i]) : 0u;
+  }
+}
+
+template <typename TIn, int GRAN, int FMT, bool Q16>
 __global__ __launch_bounds__(kThreads) void cast_tok_rows_kernel(
     const TIn *__restrict__ x, int64_t cols, int64_t xs_row, uint8_t *__restrict__ q, int64_t q_ld,
     void *__restrict__ sf, int64_t sf_s_row, int64_t sf_s_grp, int64_t steps_per_row, int64_t tasks,
     int64_t tasks_per_wave) {
-  constexpr int L = GRAN / 8;  // lanes per group
+  constexpr int L = GRAN / kTokEl;  // lanes per group
   constexpr int U = 4;
   constexpr bool kUe8m0 = FMT != kSfFp32;
   const int lane = threadIdx.x & 63;
@@ -72,7 +109,7 @@ __global__ __launch_bounds__(kThreads) void cast_tok_rows_kernel(
   const int64_t t_end = min(t_begin + tasks_per_wave, tasks);
 
   for (int64_t tb = t_begin; tb < t_end; tb += U) {
-    float v[U][8];
+    Raw16<TIn> raw[U];
     int64_t row[U], col[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -83,37 +120,45 @@ __global__ __launch_bounds__(kThreads) void cast_tok_rows_kernel(
         const int64_t r = t / steps_per_row;
         const int64_t s = t - r * steps_per_row;
         row[u] = r;
-        col[u] = (s * kWave + lane) * 8;
+        col[u] = s * kTokSpan + (int64_t)lane * kTokEl;
       }
-      const bool live = col[u] < cols;
-      const bool full = col[u] + 8 <= cols;
-      if (live) {
-        load8<TIn>(x + row[u] * xs_row + col[u], full, (int)(cols - col[u]), v[u]);
+      if (col[u] < cols) {
+        load16<TIn>(x + row[u] * xs_row + col[u], col[u] + kTokEl <= cols, (int)min<int64_t>(cols - col[u], kTokEl), raw[u]);
       } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[u][e] = 0.0f;
+        for (int i = 0; i < Raw16<TIn>::kWords; ++i) raw[u].w[i] = 0u;
       }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (tb + u >= t_end) break;  // uniform across the wave
+      float v[kTokEl];
+#pragma unroll
+      for (int e = 0; e < kTokEl; ++e) v[e] = raw[u].get(e);
       uint32_t am = 0;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) am = max(am, abs_bits(v[u][e]));
+      for (int e = 0; e < kTokEl; ++e) am = max(am, abs_bits(v[e]));
       am = group_max_u32<L>(am);
       const GroupScale gs = group_scale<kUe8m0>(__uint_as_float(am));
       const float mu = gs.mult;
-      const uint32_t w0 = e4m3x4(v[u][0] * mu, v[u][1] * mu, v[u][2] * mu, v[u][3] * mu);
-      const uint32_t w1 = e4m3x4(v[u][4] * mu, v[u][5] * mu, v[u][6] * mu, v[u][7] * mu);
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        w[e] = e4m3x4(v[4 * e] * mu, v[4 * e + 1] * mu, v[4 * e + 2] * mu, v[4 * e + 3] * mu);
       const int64_t c = col[u];
       uint8_t *qp = q + row[u] * q_ld + c;
-      if (c + 8 <= cols) {
-        *reinterpret_cast<uint2 *>(qp) = make_uint2(w0, w1);
+      if (c + kTokEl <= cols) {
+        if constexpr (Q16) {
+          *reinterpret_cast<uint4 *>(qp) = make_uint4(w[0], w[1], w[2], w[3]);
+        } else {
+          reinterpret_cast<uint2 *>(qp)[0] = make_uint2(w[0], w[1]);
+          reinterpret_cast<uint2 *>(qp)[1] = make_uint2(w[2], w[3]);
+        }
       } else if (c < cols) {
         const int valid = (int)(cols - c);
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (e < valid) qp[e] = (uint8_t)((e < 4 ? w0 >> (8 * e) : w1 >> (8 * (e - 4))) & 0xFFu);
+        for (int e = 0; e < kTokEl; ++e)
+          if (e < valid) qp[e] = (uint8_t)((w[e >> 2] >> (8 * (e & 3))) & 0xFFu);
       }
       const int64_t g = c / GRAN;  // group of this lane
       if constexpr (FMT != kSfPackedUe8m0) {
@@ -123,12 +168,14 @@ __global__ __launch_bounds__(kThreads) void cast_tok_rows_kernel(
         const uint32_t mine = c < cols ? gs.e8 << (8 * (g & 3)) : 0u;
         uint32_t word;
         if constexpr (GRAN == 32) {
-          word = group_or_u32<16>(mine);
+          word = group_or_u32<8>(mine);   // 4 groups x 2 lanes
         } else {
-          word = (uint32_t)__builtin_amdgcn_readlane((int)mine, 0) |
-                 (uint32_t)__builtin_amdgcn_readlane((int)mine, 16) |
-                 (uint32_t)__builtin_amdgcn_readlane((int)mine, 32) |
-                 (uint32_t)__builtin_amdgcn_readlane((int)mine, 48);
+          const uint32_t r16 = group_or_u32<16>(mine);   // 2 groups x 8 lanes per 16-lane row
+          const int base = lane & 32;                      // lanes 0-31 -> word 2s, 32-63 -> word 2s+1
+          word = (uint32_t)__builtin_amdgcn_readlane((int)r16, 0) | (uint32_t)__builtin_amdgcn_readlane((int)r16, 16);
+          const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)r16, 32) |
+                              (uint32_t)__builtin_amdgcn_readlane((int)r16, 48);
+          if (base) word = hi;
         }
         if ((lane % (4 * L)) == 0 && c < cols)
           reinterpret_cast<uint32_t *>(sf)[row[u] * sf_s_row + (g >> 2) * sf_s_grp] = word;
@@ -369,16 +416,22 @@ __global__ __launch_bounds__(kThreads) void cast_block_kernel(
 template <typename TIn, int GRAN, int FMT>
 hipError_t launch_tok_rows(const void *x, int64_t rows, int64_t cols, int64_t xs_row, uint8_t *q,
                            int64_t q_ld, void *sf, int64_t sf_s_row, int64_t sf_s_grp, hipStream_t st) {
-  const int64_t steps = (cols + 511) / 512;
+  const int64_t steps = (cols + kTokSpan - 1) / kTokSpan;
   const int64_t tasks = rows * steps;
-  const int64_t target_waves = 8192;  // ~8 workgroups of 4 waves per CU
+  const int64_t target_waves = 16384;  // 16 waves per CU in flight
   int64_t tpw = (tasks + target_waves - 1) / target_waves;
   if (tpw < 1) tpw = 1;
   const int64_t waves = (tasks + tpw - 1) / tpw;
   const int64_t blocks = (waves + 3) / 4;
-  hipLaunchKernelGGL((cast_tok_rows_kernel<TIn, GRAN, FMT>), dim3((unsigned)blocks), dim3(kThreads), 0, st,
-                     reinterpret_cast<const TIn *>(x), cols, xs_row, q, q_ld, sf, sf_s_row, sf_s_grp, steps,
-                     tasks, tpw);
+  const bool q16 = (reinterpret_cast<uintptr_t>(q) % 16 == 0) && (q_ld % 16 == 0);
+  if (q16)
+    hipLaunchKernelGGL((cast_tok_rows_kernel<TIn, GRAN, FMT, true>), dim3((unsigned)blocks), dim3(kThreads), 0, st,
+                       reinterpret_cast<const TIn *>(x), cols, xs_row, q, q_ld, sf, sf_s_row, sf_s_grp, steps, tasks,
+                       tpw);
+  else
+    hipLaunchKernelGGL((cast_tok_rows_kernel<TIn, GRAN, FMT, false>), dim3((unsigned)blocks), dim3(kThreads), 0, st,
+                       reinterpret_cast<const TIn *>(x), cols, xs_row, q, q_ld, sf, sf_s_row, sf_s_grp, steps, tasks,
+                       tpw);
   return hipGetLastError();
 }
 
