@@ -106,7 +106,7 @@ int cast_per_token(const void *x, int x_dtype, int64_t rows, int64_t cols,
  * x       bf16 or fp32 [rows, cols] row-major, leading dimension x_ld >= cols
  *         (elements); 16-byte aligned, x_ld a multiple of 16 bytes.
  * sf_fmt  FGFP8_SF_FP32 or FGFP8_SF_UE8M0 (fp32 holding 2^e).
- * q       E4M3 [rows, cols], ld q_ld >= cols, multiple of 16; q 16-B aligned.
+ * q       E4M3 [rows, cols], ld q_ld >= cols, multiple of 8; q 8-B aligned.
  * sf      fp32 [ceil(rows/128), ceil(cols/128)], block (bi, bj) at
  *         sf[bi*sf_ld + bj], sf_ld >= ceil(cols/128).
  * qT      NULL, or E4M3 [cols, rows] = q^T, ld qT_ld >= rows, multiple of 16.
