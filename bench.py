@@ -13,7 +13,9 @@ in=7168, out=4096, bf16 randn inputs, 1x128 / 128x128 fp32 scales):
 `value` is the step's GEMM work (3 x 2*8192*4096*7168 flop) over the whole
 step time, casts included.  Per-kernel times come from HIP events recorded
 on the launch stream inside the timed region.  Extra kernel measurements
-(the 16384x4096 cast, the 4096x7168x7168 GEMM) run after the timed region.
+(16384x4096 casts, the 1..16384-token cast sweep, prefill and decode GEMMs)
+run after the timed region; `cpu_baseline` times the oracle on a bounded
+sample of the same step.
 """
 from __future__ import annotations
 
@@ -38,6 +40,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--calibration-copy", type=int, default=0, metavar="MIB",
+                    help="first run one plain device copy of MIB MiB (a kernel of known HBM traffic "
+                         "for scaling hardware byte counters)")
     return ap.parse_args()
 
 
@@ -121,72 +126,179 @@ def rate(unit, amount, ms):
     return {"ms": ms, "gbs": v, "frac_hbm_peak": v / PEAK_HBM_GBS}
 
 
+def _quantiles(ts):
+    v = sorted(ts)
+    q = lambda f: v[min(len(v) - 1, int(f * len(v)))]
+    return q(0.5), q(0.1), q(0.9)
+
+
+def _time(torch, fn, reps=20, warm=3):
+    """Median / p10 / p90 of `reps` event-timed launches on the current stream."""
+    for _ in range(warm):
+        fn()
+    ts = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        ts.append((a, b))
+    torch.cuda.synchronize()
+    return _quantiles([a.elapsed_time(b) for a, b in ts])
+
+
+def _time_graph(torch, fn, reps=20):
+    """Per-launch time of `reps` launches captured in one HIP graph (one replay)."""
+    fn()
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for _ in range(reps):
+                fn()
+    torch.cuda.current_stream().wait_stream(s)
+    g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def _measure(torch, unit, amount, fn, reps=20):
+    """Rate from the per-launch time of `reps` graph-captured launches (no host gaps:
+    a small kernel's eager time is mostly launch overhead), plus the eager median,
+    p10 and p90 of `reps` event-timed launches."""
+    q = _time(torch, fn, reps)
+    g = _time_graph(torch, fn, reps)
+    r = rate(unit, amount, g)
+    r["eager_ms"], r["eager_p10_ms"], r["eager_p90_ms"] = q
+    return r
+
+
+def _gemm_operands(fg, torch, si, m, n, k):
+    """randn*0.1 operands cast on the GPU: A per token (1x128 fp32, MN-major), B per 128x128 block."""
+    a = si.randn((m, k), si.SEED_A, 0.1).cuda()
+    b = si.randn((n, k), si.SEED_B, 0.1).cuda()
+    A = torch.empty((m, k), dtype=torch.uint8, device="cuda")
+    sa = fg.mn_major_scales(m, k // 128)
+    fg.cast_per_token(a, A, sa, 128, fg.SF_FP32)
+    B = torch.empty((n, k), dtype=torch.uint8, device="cuda")
+    sb = torch.empty((-(-n // 128), k // 128), dtype=torch.float32, device="cuda")
+    fg.cast_per_block(b, B, sb, sf_fmt=fg.SF_FP32)
+    D = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    torch.cuda.synchronize()
+    return A, sa, B, sb, D
+
+
 def extra_kernels(fg, torch, si):
-    """Single-kernel measurements outside the timed step (fresh buffers, median of 20)."""
+    """Single-kernel measurements outside the timed step: median (p10, p90) of 20 event-timed
+    launches; inputs that must come from HBM rotate over buffers larger than L2 + MALL."""
     out = {}
-
-    def med(fn, reps=20):
-        ts = []
-        for _ in range(3):
-            fn()
-        for _ in range(reps):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            fn()
-            b.record()
-            ts.append((a, b))
-        torch.cuda.synchronize()
-        v = sorted(a.elapsed_time(b) for a, b in ts)
-        return v[len(v) // 2]
-
-    # 16384 x 4096 per-token casts (group 128 fp32 scales; group 32 packed UE8M0)
+    # 16384 x 4096 per-token casts (group 128 fp32 scales; group 32 packed UE8M0), 3 inputs rotated
     rows, cols = 16384, 4096
-    xs = [si.randn((rows, cols), s).cuda() for s in range(3)]          # rotate > L2 + MALL
+    xs = [si.randn((rows, cols), s).cuda() for s in range(3)]
     q = torch.empty((rows, cols), dtype=torch.uint8, device="cuda")
     for gran, fmt, name in ((128, fg.SF_FP32, "cast_16384x4096_g128_fp32"),
+                            (32, fg.SF_FP32, "cast_16384x4096_g32_fp32"),
                             (32, fg.SF_PACKED_UE8M0, "cast_16384x4096_g32_packed")):
         G = cols // gran
-        sf = fg.mn_major_scales(rows, -(-G // 4) if fmt == fg.SF_PACKED_UE8M0 else G,
-                                torch.int32 if fmt == fg.SF_PACKED_UE8M0 else torch.float32)
+        units = -(-G // 4) if fmt == fg.SF_PACKED_UE8M0 else G
+        sf = fg.mn_major_scales(rows, units, torch.int32 if fmt == fg.SF_PACKED_UE8M0 else torch.float32)
         it = iter(range(1 << 30))
-        ms = med(lambda: fg.cast_per_token(xs[next(it) % 3], q, sf, gran, fmt))
-        units = sf.shape[1]
-        nbytes = rows * cols * 3 + rows * units * 4
-        out[name] = rate("GB/s", nbytes, ms)
+        out[name] = _measure(torch, "GB/s", rows * cols * 3 + rows * units * 4,
+                             lambda: fg.cast_per_token(xs[next(it) % 3], q, sf, gran, fmt))
     del xs
-    # prefill GEMM 4096 x 7168 x 7168
-    for (m, n, k) in ((4096, 7168, 7168), (4096, 4096, 7168)):
-        A = torch.randint(0, 0x70, (m, k), dtype=torch.uint8, device="cuda")
-        B = torch.randint(0, 0x70, (n, k), dtype=torch.uint8, device="cuda")
-        sa = fg.mn_major_scales(m, k // 128)
-        sa.fill_(0.01)
-        sb = torch.full((n // 128, k // 128), 0.01, dtype=torch.float32, device="cuda")
-        D = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
-        ms = med(lambda: fg.gemm_fp8_nt_bf16(A, sa, B, sb, D))
-        out[f"gemm_{m}x{n}x{k}"] = rate("TFLOPS", 2.0 * m * n * k, ms)
+    # token sweep of the fused-cast table (hidden 4096, g32, packed UE8M0): eager and graph-captured
+    sweep = {}
+    for t in (1, 64, 512, 4096, 16384):
+        x = si.randn((t, 4096), si.SEED_A).cuda()
+        qt = torch.empty((t, 4096), dtype=torch.uint8, device="cuda")
+        sf = fg.mn_major_scales(t, 32, torch.int32)
+        qs = _time(torch, lambda: fg.cast_per_token(x, qt, sf, 32, fg.SF_PACKED_UE8M0))
+        gms = _time_graph(torch, lambda: fg.cast_per_token(x, qt, sf, 32, fg.SF_PACKED_UE8M0))
+        nbytes = t * 4096 * 3 + t * 32 * 4
+        sweep[str(t)] = {"eager_us": qs[0] * 1e3, "graph_us": gms * 1e3,
+                         "graph_gbs": nbytes / (gms * 1e-3) / 1e9}
+        del x, qt, sf
+    out["cast_token_sweep_4096_g32_packed"] = sweep
+    # prefill and decode GEMMs on randn*0.1 operands; a decode GEMM reads B once, so
+    # 12 copies of B (> 256 MiB) rotate to keep it coming from HBM
+    for (m, n, k) in list(si.GEMM_PREFILL) + list(si.GEMM_DECODE):
+        A, sa, B, sb, D = _gemm_operands(fg, torch, si, m, n, k)
+        Bs = [B] if m > 512 else [B] + [B.clone() for _ in range(11)]
+        it = iter(range(1 << 30))
+        r = _measure(torch, "TFLOPS", 2.0 * m * n * k,
+                     lambda: fg.gemm_fp8_nt_bf16(A, sa, Bs[next(it) % len(Bs)], sb, D))
+        nbytes = m * k + n * k + m * (k // 128) * 4 + sb.numel() * 4 + m * n * 2
+        r["gbs"] = nbytes / (r["ms"] * 1e-3) / 1e9
+        r["frac_hbm_peak"] = r["gbs"] / PEAK_HBM_GBS
+        out[f"gemm_{m}x{n}x{k}"] = r
+        del A, sa, B, sb, D, Bs
     return out
 
 
-def cpu_baseline(si):
-    """The oracle, as it stands, on a bounded sample of the same step: the forward
-    GEMM for 128 tokens x 1024 output features (k = 7168) plus the per-token cast of
-    those 128 tokens.  Reported in the step metric's unit (GEMM TFLOPS)."""
+def cpu_baseline(si, target_s=20.0):
+    """The oracle, as it stands, on a bounded sample of the same step: one complete
+    linear step (casts, forward, dgrad, wgrad) at in=7168, out=4096 and T tokens, T a
+    multiple of 128 sized from a 128-token calibration run so that the sample takes
+    about `target_s` seconds.  Reported in the step metric's unit (GEMM TFLOPS)."""
     import numpy as np
     import oracle
     threads = len(os.sched_getaffinity(0))
     oracle.set_threads(threads)
-    T, I, Osub = 128, 7168, 1024
-    x = si.randn((T, I), si.SEED_A)
-    W = si.randn((Osub, I), si.SEED_B)
-    t0 = time.perf_counter()
-    qa, sa = oracle.cast_per_token(si.host_array(x), 128, oracle.SF_FP32)
-    qb, sb = oracle.cast_per_block(si.host_array(W), oracle.SF_FP32)
-    ref, _ = oracle.gemm_nt(qa, sa, qb, sb)
-    dt = time.perf_counter() - t0
-    flops = 2.0 * T * I * Osub
+    I, O = si.LINEAR["d_in"], si.LINEAR["d_out"]
+
+    def step(T):
+        x = si.host_array(si.randn((T, I), si.SEED_A))
+        W = si.host_array(si.randn((O, I), si.SEED_B))
+        dy = si.host_array(si.randn((T, O), si.SEED_DY))
+        t0 = time.perf_counter()
+        qx, sx = oracle.cast_per_token(x, 128, oracle.SF_FP32)
+        qw, sw = oracle.cast_per_block(W, oracle.SF_FP32)
+        oracle.gemm_nt(qx, sx, qw, sw)
+        qd, sd = oracle.cast_per_token(dy, 128, oracle.SF_FP32)
+        oracle.gemm_nt(qd, sd, np.ascontiguousarray(qw.T), np.ascontiguousarray(sw.T))
+        qdT, sdT = oracle.cast_per_token(dy, 128, oracle.SF_FP32, transpose=True)
+        qxT, sxT = oracle.cast_per_token(x, 128, oracle.SF_FP32, transpose=True)
+        oracle.wgrad_nt(qdT, sdT, qxT, sxT, np.zeros((O, I), np.float32))
+        return time.perf_counter() - t0
+
+    cal = step(128)
+    T = int(min(si.LINEAR["tokens"], max(128, 128 * round(target_s / cal))))
+    dt = step(T)
+    flops = 3 * 2.0 * T * I * O
     return {"value": flops / dt / 1e12, "unit": "TFLOPS", "cores": oracle.max_threads(), "kind": "oracle",
-            "sample": f"forward GEMM {T}x{Osub}x{I} (fp64 exact block sums) + casts of its operands; "
-                      f"{dt:.2f} s"}
+            "sample": f"one full linear step (per-token and block casts, forward, dgrad, wgrad; fp64 exact "
+                      f"block sums) at {T} of the 8192 tokens, in=7168, out=4096: {dt:.1f} s"}
+
+
+def _source_digest(files):
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "fine_grained_block_token_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(op):
+    """HBM bytes per launch of `op` from the committed counter summary (FETCH_SIZE and
+    WRITE_SIZE, scaled by a copy of known size), or None when the summary is missing or
+    the kernel's sources have changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_fp8_linear_step.md")
+    try:
+        text = open(path).read()
+        data = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
+        entry = data["ops"][op]
+    except (OSError, IndexError, KeyError, ValueError):
+        return None
+    files = ["gemm.hip" if op.startswith("gemm") else "cast.hip", "device_common.h", "launch.h"]
+    return entry["traffic_bytes"] if entry["source"] == _source_digest(files) else None
 
 
 def main():
@@ -200,6 +312,13 @@ def main():
     import synth_inputs as si
     fg.load()
     torch.cuda.set_device(0)
+    if args.calibration_copy:
+        src = torch.ones(args.calibration_copy << 18, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     cfg = si.LINEAR
     lin = Linear(fg, torch, si, cfg["tokens"], cfg["d_in"], cfg["d_out"])
     ops = lin.ops()
@@ -228,7 +347,9 @@ def main():
                    "tokens": cfg["tokens"], "d_in": cfg["d_in"], "d_out": cfg["d_out"],
                    "gran_k": 128, "scales": "fp32", "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": dom_tflops, "peak": PEAK_FP8_TFLOPS,
-                     "unit": "TFLOP/s", "frac": dom_tflops / PEAK_FP8_TFLOPS, "traffic": None},
+                     "unit": "TFLOP/s", "frac": dom_tflops / PEAK_FP8_TFLOPS, "traffic": measured_traffic(dom),
+                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                     "algorithmic_flop_per_launch": work[dom][1]},
         "kernels": kernels,
     }
     if not args.no_extra:

@@ -109,6 +109,7 @@ static int check_gemm_common(const uint8_t *A, int64_t lda, const void *sa, int6
   if (!aligned(A, 16) || lda < k || lda % 16 != 0) return FGFP8_EINVAL;
   if (!aligned(B, 16) || ldb < k || ldb % 16 != 0) return FGFP8_EINVAL;
   if (!aligned(sa, 4) || !aligned(sb, 4) || sa_ld < m) return FGFP8_EINVAL;
+  if (lda >= (int64_t)1 << 24 || ldb >= (int64_t)1 << 24) return FGFP8_EINVAL;  // 32-bit in-tile offsets
   if (cdiv(m, 128) > 0x7FFFFFFF || cdiv(n, 128) > 0x7FFFFFFF) return FGFP8_EINVAL;
   return 1;  // proceed
 }

@@ -94,15 +94,16 @@ __device__ __forceinline__ v4f mfma_k128(v8i a, v8i b) {
 typedef const void __attribute__((address_space(1))) *gptr_t;
 typedef void __attribute__((address_space(3))) *lptr_t;
 
-// 64 lanes x 16 bytes global -> LDS; the LDS destination of lane l is dst + 16*l
-// (dst is wave-uniform and goes to M0).  Issued as inline assembly so that the
-// compiler's wait insertion does not treat every later LDS read as possibly
-// aliasing the copy in flight; the kernel orders these copies with explicit
-// s_waitcnt vmcnt + s_barrier.
-__device__ __forceinline__ void load_lds16(const uint8_t *src, uint8_t *dst_wave) {
+// 64 lanes x 16 bytes global -> LDS: lane l reads base + off (base wave-uniform,
+// held in SGPRs; off a 32-bit per-lane offset) and its 16 bytes land at
+// dst + 16*l (dst is wave-uniform and goes to M0).  Issued as inline assembly so
+// that the compiler's wait insertion does not treat every later LDS read as
+// possibly aliasing the copy in flight; the kernel orders these copies with
+// explicit s_waitcnt vmcnt + s_barrier.
+__device__ __forceinline__ void load_lds16(const void *base, uint32_t off, uint8_t *dst_wave) {
   const uint32_t lds = (uint32_t)(uintptr_t)(lptr_t)dst_wave;
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               ::"v"(src), "s"(lds) : "memory", "m0");
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               ::"v"(off), "s"(base), "s"(lds) : "memory", "m0");
 }
 
 template <int SA_FMT>
@@ -122,10 +123,11 @@ struct BlockScales {
   v4f sbj[4];       // wgrad: per column-subtile, 4 consecutive columns
 };
 
-__device__ __forceinline__ void load_lds4(const void *src, uint8_t *dst_wave) {
+// As load_lds16 with 4 bytes per lane (lane l's dword lands at dst + 4*l).
+__device__ __forceinline__ void load_lds4(const void *base, uint32_t off, uint8_t *dst_wave) {
   const uint32_t lds = (uint32_t)(uintptr_t)(lptr_t)dst_wave;
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
-               ::"v"(src), "s"(lds) : "memory", "m0");
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+               ::"v"(off), "s"(base), "s"(lds) : "memory", "m0");
 }
 
 // acc += P * scale for MFMA tile (mi, ni)
@@ -163,7 +165,8 @@ __global__ __launch_bounds__(C::kThreads, 2) void gemm_kernel(GemmArgs g, int ti
   const int64_t m = g.m, n = g.n;
   const int KB = (int)(g.k / kBK);
 
-  // Direct-to-LDS copy of one stage (tiles and scales of one K block).  Each 1 KB
+  // Direct-to-LDS copy of one stage (tiles and scales of one K block).  Offsets
+  // are 32-bit from the tile's first row (the host bounds lda, ldb < 2^24).  Each 1 KB
   // wave instruction fills 64 consecutive 16-byte slots; slot s holds row s/8,
   // physical chunk s%8, i.e. logical chunk (s%8) ^ swz_key(row).  Wave wv issues
   // tile instructions wv, wv + kWaves, ...; the scale rows (4 bytes per lane) are
@@ -172,36 +175,36 @@ __global__ __launch_bounds__(C::kThreads, 2) void gemm_kernel(GemmArgs g, int ti
 #pragma unroll
   for (int i = 0; i < C::kALoads; ++i) {
     const int s = 64 * (i * C::kWaves + wv) + lane, row = s >> 3, chunk = (s & 7) ^ swz_key(row);
-    a_off[i] = (uint32_t)(min(m0 + row, m - 1) * g.lda) + (uint32_t)(chunk * 16);
+    a_off[i] = (uint32_t)(min((int64_t)row, m - 1 - m0) * g.lda) + (uint32_t)(chunk * 16);
   }
 #pragma unroll
   for (int i = 0; i < C::kBLoads; ++i) {
     const int s = 64 * (i * C::kWaves + wv) + lane, row = s >> 3, chunk = (s & 7) ^ swz_key(row);
-    b_off[i] = (uint32_t)(min(n0 + row, n - 1) * g.ldb) + (uint32_t)(chunk * 16);
+    b_off[i] = (uint32_t)(min((int64_t)row, n - 1 - n0) * g.ldb) + (uint32_t)(chunk * 16);
   }
   static_assert(C::kSaLoads + C::kSbLoads <= C::kWaves, "one scale load per wave at most");
   const bool sa_loader = wv < C::kSaLoads;
   const bool sb_loader = wv >= C::kSaLoads && wv < C::kSaLoads + C::kSbLoads;
-  int64_t scale_row;   // row of sa (or column of sb) this lane copies
-  if (sa_loader) {
-    scale_row = min(m0 + 64 * wv + lane, m - 1);
-  } else {
-    scale_row = min(n0 + 64 * (wv - C::kSaLoads) + lane, n - 1);
-  }
+  // row of sa (or column of sb) this lane copies, relative to the tile's first
+  const uint32_t scale_off = sa_loader ? 4u * (uint32_t)min((int64_t)(64 * wv + lane), m - 1 - m0)
+                                       : 4u * (uint32_t)min((int64_t)(64 * (wv - C::kSaLoads) + lane), n - 1 - n0);
   auto issue = [&](int kb, uint8_t *st) {
-    const uint8_t *ga = g.A + (int64_t)kb * kBK;
-    const uint8_t *gb = g.B + (int64_t)kb * kBK;
+    const uint8_t *ga = g.A + m0 * g.lda + (int64_t)kb * kBK;
+    const uint8_t *gb = g.B + n0 * g.ldb + (int64_t)kb * kBK;
 #pragma unroll
-    for (int i = 0; i < C::kALoads; ++i) load_lds16(ga + a_off[i], st + 1024 * (i * C::kWaves + wv));
+    for (int i = 0; i < C::kALoads; ++i) load_lds16(ga, a_off[i], st + 1024 * (i * C::kWaves + wv));
 #pragma unroll
-    for (int i = 0; i < C::kBLoads; ++i) load_lds16(gb + b_off[i], st + C::kABytes + 1024 * (i * C::kWaves + wv));
+    for (int i = 0; i < C::kBLoads; ++i) load_lds16(gb, b_off[i], st + C::kABytes + 1024 * (i * C::kWaves + wv));
     if (sa_loader) {
       const int64_t col = SA_FMT == kSfPackedUe8m0 ? (kb >> 2) : kb;
-      load_lds4(reinterpret_cast<const uint32_t *>(g.sa) + col * g.sa_ld + scale_row, st + C::kSaOff + 256 * wv);
+      load_lds4(reinterpret_cast<const uint32_t *>(g.sa) + col * g.sa_ld + m0, scale_off,
+                st + C::kSaOff + 256 * wv);
     } else if (sb_loader) {
-      const float *src = WGRAD ? g.sb + (int64_t)kb * g.sb_ld + scale_row
-                               : g.sb + (n0 >> 7) * g.sb_ld + kb;   // forward: the tile's one block scale
-      load_lds4(src, st + C::kSbOff + 256 * (wv - C::kSaLoads));
+      if constexpr (WGRAD) {
+        load_lds4(g.sb + (int64_t)kb * g.sb_ld + n0, scale_off, st + C::kSbOff + 256 * (wv - C::kSaLoads));
+      } else {   // forward: the tile's one block scale, the same dword in every lane
+        load_lds4(g.sb + (n0 >> 7) * g.sb_ld + kb, 0u, st + C::kSbOff + 256 * (wv - C::kSaLoads));
+      }
     }
   };
   auto read_scales = [&](int kb, const uint8_t *st, BlockScales &s) {
@@ -322,6 +325,125 @@ __global__ __launch_bounds__(C::kThreads, 2) void gemm_kernel(GemmArgs g, int ti
   }
 }
 
+// Skinny (decode-sized) problems, m <= 16*MT: there is too little output to fill
+// 256 CUs with 128x128 tiles (m = 1, n = 7168 gives 56 tiles), and the time goes
+// into streaming B once from HBM.  A workgroup owns 16*NT columns (inside one
+// 128-column block, so one RHS block scale per K block) and all 16*MT rows; its W
+// waves take the K blocks round-robin (wave w: blocks w, w + W, ...), load their
+// fragments straight into VGPRs through a DEPTH-deep register ring (no LDS
+// staging: nothing is reused across waves) and keep their own promoted fp32
+// accumulators.  The W partial accumulators are then added through LDS in wave
+// order, so the result does not depend on scheduling.
+template <int MT, int NT, int W, int DEPTH, int SA_FMT>
+__global__ __launch_bounds__(64 * W) void gemm_skinny_kernel(GemmArgs g, int tiles_n) {
+  static_assert(128 % (16 * NT) == 0, "a workgroup's columns lie in one 128-column block");
+  __shared__ v4f red[W][MT * NT][64];
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tn = (int)(blockIdx.x % tiles_n), tm = (int)(blockIdx.x / tiles_n);
+  const int64_t m0 = (int64_t)tm * 16 * MT, n0 = (int64_t)tn * 16 * NT;
+  const int64_t m = g.m, n = g.n;
+  const int KB = (int)(g.k / kBK);
+  const int koff = 32 * (lane >> 4);   // this lane's K bytes within a block (frag() layout)
+
+  const uint8_t *pa[MT];
+  bool va[MT];
+  int64_t ra[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    const int64_t row = m0 + 16 * t + (lane & 15);
+    va[t] = row < m;
+    ra[t] = min(row, m - 1);
+    pa[t] = g.A + ra[t] * g.lda + koff;
+  }
+  const uint8_t *pb[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) pb[t] = g.B + min(n0 + 16 * t + (lane & 15), n - 1) * g.ldb + koff;
+  const float *psb = g.sb + (n0 >> 7) * g.sb_ld;
+
+  struct Blk {
+    v8i a[MT], b[NT];
+    float sa[MT], sb;
+  };
+  auto load = [&](int kb, Blk &x) {
+    const int64_t o = (int64_t)kb * kBK;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const u32x4 lo = *reinterpret_cast<const u32x4 *>(pb[t] + o);
+      const u32x4 hi = *reinterpret_cast<const u32x4 *>(pb[t] + o + 16);
+      x.b[t] = (v8i){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    }
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      x.a[t] = (v8i){0, 0, 0, 0, 0, 0, 0, 0};
+      if (va[t]) {
+        const u32x4 lo = *reinterpret_cast<const u32x4 *>(pa[t] + o);
+        const u32x4 hi = *reinterpret_cast<const u32x4 *>(pa[t] + o + 16);
+        x.a[t] = (v8i){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      }
+      x.sa[t] = load_sa<SA_FMT>(g.sa, g.sa_ld, ra[t], kb);
+    }
+    x.sb = psb[kb];
+  };
+
+  v4f acc[MT * NT];
+#pragma unroll
+  for (int i = 0; i < MT * NT; ++i) acc[i] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+  auto compute = [&](const Blk &x) {
+#pragma unroll
+    for (int tm_ = 0; tm_ < MT; ++tm_) {
+      const float c = x.sa[tm_] * x.sb;
+#pragma unroll
+      for (int tn_ = 0; tn_ < NT; ++tn_) {
+        const v4f p = mfma_k128(x.b[tn_], x.a[tm_]);
+        v4f &a = acc[tm_ * NT + tn_];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) a[r] = __builtin_fmaf(p[r], c, a[r]);
+      }
+    }
+  };
+
+  // Register ring: block j of this wave (kb = wv + j*W) lives in buf[j % DEPTH];
+  // loads run DEPTH - 1 blocks ahead of the MFMAs.
+  const int nblk = wv < KB ? (KB - 1 - wv) / W + 1 : 0;
+  Blk buf[DEPTH];
+#pragma unroll
+  for (int d = 0; d < DEPTH - 1; ++d)
+    if (d < nblk) load(wv + d * W, buf[d]);
+  for (int j0 = 0; j0 < nblk; j0 += DEPTH) {
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+      const int j = j0 + d;
+      if (j < nblk) {
+        const int jn = j + DEPTH - 1;
+        if (jn < nblk) load(wv + jn * W, buf[(d + DEPTH - 1) % DEPTH]);
+        compute(buf[d]);
+      }
+    }
+  }
+
+#pragma unroll
+  for (int i = 0; i < MT * NT; ++i) red[wv][i][lane] = acc[i];
+  __syncthreads();
+  for (int i = wv; i < MT * NT; i += W) {
+    v4f sum = red[0][i][lane];
+#pragma unroll
+    for (int w = 1; w < W; ++w) sum += red[w][i][lane];
+    const int64_t row = m0 + 16 * (i / NT) + (lane & 15);
+    const int64_t col = n0 + 16 * (i % NT) + 4 * (lane >> 4);
+    if (row >= m || col >= n) continue;
+    uint16_t *dp = reinterpret_cast<uint16_t *>(g.D) + row * g.ldd + col;
+    if (col + 4 <= n) {
+      *reinterpret_cast<u32x2 *>(dp) = (u32x2){bf16_rne(sum[0]) | (bf16_rne(sum[1]) << 16),
+                                               bf16_rne(sum[2]) | (bf16_rne(sum[3]) << 16)};
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (col + r < n) dp[r] = (uint16_t)bf16_rne(sum[r]);
+    }
+  }
+}
+
 }  // namespace
 
 template <class C>
@@ -340,7 +462,26 @@ hipError_t launch_cfg(const GemmArgs &a, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <int MT, int NT, int W, int DEPTH>
+hipError_t launch_skinny(const GemmArgs &a, hipStream_t st) {
+  const int tiles_n = (int)((a.n + 16 * NT - 1) / (16 * NT));
+  const int tiles_m = (int)((a.m + 16 * MT - 1) / (16 * MT));
+  const dim3 grid((unsigned)(tiles_n * tiles_m));
+  if (a.sa_fmt == kSfPackedUe8m0) {
+    hipLaunchKernelGGL((gemm_skinny_kernel<MT, NT, W, DEPTH, kSfPackedUe8m0>), grid, dim3(64 * W), 0, st, a, tiles_n);
+  } else {
+    hipLaunchKernelGGL((gemm_skinny_kernel<MT, NT, W, DEPTH, kSfFp32>), grid, dim3(64 * W), 0, st, a, tiles_n);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm(const GemmArgs &a, hipStream_t st) {
+  if (!a.wgrad && a.m <= 64) {
+    // decode-sized: stream B with K split over the waves of a workgroup
+    if (a.m <= 16) return launch_skinny<1, 1, 8, 4>(a, st);
+    if (a.m <= 32) return launch_skinny<2, 2, 8, 2>(a, st);
+    return launch_skinny<4, 2, 8, 2>(a, st);
+  }
   // 128x128 output tiles, 4 waves, 2 LDS stages (66 KB): two workgroups per CU, so
   // one workgroup's barrier and copy latency is covered by the other's MFMAs.
   return launch_cfg<Cfg<2, 2, 2>>(a, st);

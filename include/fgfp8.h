@@ -129,12 +129,12 @@ int cast_per_block(const void *x, int x_dtype, int64_t rows, int64_t cols, int64
  * sa(i, kb) * sb(j/128, kb) and added to an fp32 accumulator; the result is
  * rounded to bf16 (nearest, ties to even).
  *
- * A       E4M3 [m, k] row-major, lda >= k, multiple of 16; 16-B aligned.
+ * A       E4M3 [m, k] row-major, k <= lda < 2^24, lda a multiple of 16; 16-B aligned.
  * sa      per-token scales in MN-major layout: sa_fmt FGFP8_SF_FP32 or
  *         FGFP8_SF_UE8M0: float (i, kb) at sa[kb*sa_ld + i];
  *         FGFP8_SF_PACKED_UE8M0: int32 word (i, kb/4) at sa[(kb/4)*sa_ld + i],
  *         exponent byte kb%4.  sa_ld >= m.
- * B       E4M3 [n, k] row-major, ldb >= k, multiple of 16; 16-B aligned.
+ * B       E4M3 [n, k] row-major, k <= ldb < 2^24, ldb a multiple of 16; 16-B aligned.
  * sb      fp32 [ceil(n/128), k/128] row-major: (nb, kb) at sb[nb*sb_ld + kb],
  *         sb_ld >= k/128.
  * D       bf16 [m, n] row-major, ldd >= n, multiple of 8; 16-B aligned.
@@ -154,9 +154,9 @@ int gemm_fp8_nt_bf16(const uint8_t *A, int64_t lda, const void *sa, int sa_fmt, 
  * tokens).  Both operands carry one scale per row and 128-wide K block; each
  * K block's fp32 partial sum is multiplied by sa(i, kb) * sb(j, kb).
  *
- * A   E4M3 [m, k] (m = output features, k = tokens), lda >= k, multiple of 16.
+ * A   E4M3 [m, k] (m = output features, k = tokens), k <= lda < 2^24, multiple of 16.
  * sa  fp32 (i, kb) at sa[kb*sa_ld + i], sa_ld >= m.
- * B   E4M3 [n, k] (n = input features), ldb >= k, multiple of 16.
+ * B   E4M3 [n, k] (n = input features), k <= ldb < 2^24, multiple of 16.
  * sb  fp32 (j, kb) at sb[kb*sb_ld + j], sb_ld >= n.
  * D   fp32 [m, n] row-major, ldd >= n, multiple of 4; read and written.
  * k must be a positive multiple of 128.

@@ -97,6 +97,7 @@ def gemm(lib, **kw):
 @pytest.mark.parametrize("kw", [
     dict(k=200), dict(k=0), dict(lda=200), dict(ldb=250), dict(sald=100), dict(sbld=1), dict(ldd=100),
     dict(ldd=252), dict(fmt=5), dict(A=None), dict(D=ctypes.c_void_p(0x10004)), dict(m=-1),
+    dict(lda=1 << 24), dict(ldb=1 << 24),
 ])
 def test_gemm_rejects(lib, kw):
     assert gemm(lib, **kw) == -1
@@ -114,6 +115,6 @@ def wgrad(lib, **kw):
                                       a["sbld"], a["D"], a["ldd"], a["m"], a["n"], a["k"], a["st"])
 
 
-@pytest.mark.parametrize("kw", [dict(sbld=100), dict(k=100), dict(ldd=254), dict(sb=None)])
+@pytest.mark.parametrize("kw", [dict(sbld=100), dict(k=100), dict(ldd=254), dict(sb=None), dict(lda=1 << 24)])
 def test_wgrad_rejects(lib, kw):
     assert wgrad(lib, **kw) == -1

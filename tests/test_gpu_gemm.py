@@ -149,6 +149,46 @@ def test_gemm_decode(gpu, m, nk):
         check_bf16_gemm(got[ii, jj], ref, absum, tb, k // 128, f"decode {(m, n, k)}")
 
 
+@pytest.mark.parametrize("m", [1, 5, 16, 17, 32, 33, 63, 64, 65])
+@pytest.mark.parametrize("nk", [(1000, 128), (200, 1152), (4096, 2176)])
+def test_gemm_skinny_edges(gpu, m, nk):
+    # decode-sized m: every row count around the 16 / 32 / 64-row configurations,
+    # ragged n, fewer K blocks than the waves that split them (k = 128) and an
+    # uneven split (9 and 17 blocks over 8 waves)
+    n, k = nk
+    qa, sa, qb, sb = _cast_operands(m, n, k, scale=0.1)
+    got = _run_gemm(qa, sa, qb, sb)
+    ref, absum = oracle.gemm_nt(qa, sa, qb, sb)
+    check_bf16_gemm(got, ref, absum, mfma_truncation_bound(qa, sa, qb, sb), k // 128, f"skinny {(m, n, k)}")
+
+
+@pytest.mark.parametrize("m", [3, 40])
+def test_gemm_skinny_packed_ue8m0(gpu, m):
+    n, k = 384, 1024
+    qa, words, qb, sb = _cast_operands(m, n, k, scale=0.1, a_fmt=oracle.SF_PACKED_UE8M0)
+    sa = oracle.unpack_ue8m0(words, k // 128)
+    got = _run_gemm(qa, words, qb, sb, sa_fmt=fg.SF_PACKED_UE8M0)
+    ref, absum = oracle.gemm_nt(qa, sa, qb, sb)
+    check_bf16_gemm(got, ref, absum, mfma_truncation_bound(qa, sa, qb, sb), k // 128, f"skinny packed m={m}")
+    assert np.array_equal(got, _run_gemm(qa, sa, qb, sb, sa_fmt=fg.SF_UE8M0))
+
+
+def test_gemm_skinny_one_hot(gpu):
+    # one-hot K positions pin the skinny path's scale indexing (row, K block, 128-column block)
+    m, n, k = 20, 300, 1280
+    rng = np.random.default_rng(5)
+    sa = rng.uniform(0.5, 2, (m, k // 128)).astype(np.float32)
+    sb = rng.uniform(0.5, 2, (3, k // 128)).astype(np.float32)
+    qa = np.zeros((m, k), np.uint8)
+    qb = np.zeros((n, k), np.uint8)
+    for i0, j0, t0 in [(0, 0, 0), (19, 299, 1279), (7, 130, 700), (16, 257, 129), (3, 128, 1151)]:
+        qa[i0, t0] = 0x38
+        qb[j0, t0] = 0x38
+    got = oracle.bf16_bits_to_f32(_run_gemm(qa, sa, qb, sb)).astype(np.float64)
+    ref, _ = oracle.gemm_nt(qa, sa, qb, sb)
+    assert np.array_equal(got, oracle.bf16_bits_to_f32(oracle.round_bf16(ref)).astype(np.float64))
+
+
 # ---------------------------------------------------------------------------
 # wgrad
 # ---------------------------------------------------------------------------

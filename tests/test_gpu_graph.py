@@ -1,0 +1,82 @@
+"""The entry points inside a captured HIP graph: every replay must reproduce the
+eager result bit for bit (the library allocates nothing, never synchronises and
+records no memset, so its launches are capturable).  The graph is replayed
+several times with the program's own eager work and synchronisations in between.
+"""
+import numpy as np
+import pytest
+import torch
+
+import fine_grained_block_token_amd as fg
+import synth_inputs as si
+from gpu_util import say
+
+pytestmark = pytest.mark.gpu
+
+
+def test_graph_replays_match_eager(gpu):
+    T, I, O = 384, 1024, 640
+    x = si.randn((T, I), si.SEED_A).cuda()
+    W = si.randn((O, I), si.SEED_B).cuda()
+    u8, f32 = torch.uint8, torch.float32
+    xq = torch.empty((T, I), dtype=u8, device="cuda")
+    sx = fg.mn_major_scales(T, I // 128)
+    xq1 = torch.empty((1, I), dtype=u8, device="cuda")
+    sx1 = fg.mn_major_scales(1, I // 128)
+    Wq = torch.empty((O, I), dtype=u8, device="cuda")
+    sW = torch.empty((O // 128, I // 128), dtype=f32, device="cuda")
+    xTq = torch.empty((I, T), dtype=u8, device="cuda")
+    sxT = fg.mn_major_scales(I, T // 128)
+    wp = torch.empty((T, I), dtype=u8, device="cuda")
+    swp = fg.mn_major_scales(T, I // 32 // 4, torch.int32)
+    y = torch.empty((T, O), dtype=torch.bfloat16, device="cuda")
+    y1 = torch.empty((1, O), dtype=torch.bfloat16, device="cuda")
+    dW = torch.empty((I, I), dtype=f32, device="cuda")
+
+    def step():
+        fg.cast_per_token(x, xq, sx, 128, fg.SF_FP32)
+        fg.cast_per_token(x[:1], xq1, sx1, 128, fg.SF_FP32)
+        fg.cast_per_token(x, wp, swp, 32, fg.SF_PACKED_UE8M0)
+        fg.cast_per_token(x.t(), xTq, sxT, 128, fg.SF_FP32)
+        fg.cast_per_block(W, Wq, sW, sf_fmt=fg.SF_FP32)
+        fg.gemm_fp8_nt_bf16(xq, sx, Wq, sW, y)
+        fg.gemm_fp8_nt_bf16(xq1, sx1, Wq, sW, y1)          # decode-sized path
+        fg.wgrad_gemm_fp8_nt_fp32(xTq, sxT, xTq, sxT, dW)  # dW += xT xT^T
+
+    outs = [xq, sx, xq1, sx1, wp, swp, xTq, sxT, Wq, sW, y, y1]
+
+    def snap():
+        return [o.cpu().clone() for o in outs], dW.cpu().clone()
+
+    def clear():
+        for o in outs + [dW]:
+            o.zero_()
+
+    say("graph: eager reference")
+    clear()
+    step()
+    torch.cuda.synchronize()
+    ref, ref_dw = snap()
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+
+    for r in range(3):
+        say("graph: replay", r)
+        clear()
+        torch.cuda.synchronize()
+        junk = torch.randn(1 << 20, device="cuda").sum()     # eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        got, got_dw = snap()
+        for a, b in zip(got, ref):
+            assert torch.equal(a, b), f"replay {r} differs from the eager result"
+        # wgrad accumulates into dW: zeroed, then one pass, on both sides
+        assert torch.equal(got_dw, ref_dw), f"replay {r}: wgrad differs"
+        del junk
