@@ -4,11 +4,11 @@
 A step is one pass of the whole hot path over one batch (tokens=8192,
 in=7168, out=4096, bf16 randn inputs, 1x128 / 128x128 fp32 scales):
 
-  forward  cast x per token; cast W per 128x128 block (+ its transpose);
+  forward  cast x per token, row-wise and transposed (groups along tokens)
+           in one read; cast W per 128x128 block (+ its transpose);
            y  = GEMM(xq, Wq)                  [8192, 4096] bf16
-  dgrad    cast dY per token;  dX = GEMM(dYq, WqT)   [8192, 7168] bf16
-  wgrad    cast dY^T and x^T per token (groups along tokens);
-           dW += GEMM(dYTq, xTq)             [4096, 7168] fp32
+  dgrad    cast dY per token, both orientations; dX = GEMM(dYq, WqT)  [8192, 7168] bf16
+  wgrad    dW += GEMM(dYTq, xTq)             [4096, 7168] fp32
 
 `value` is the step's GEMM work (3 x 2*8192*4096*7168 flop) over the whole
 step time, casts included.  Per-kernel times come from HIP events recorded
@@ -69,16 +69,26 @@ class Linear:
         self.dW = torch.zeros((d_out, d_in), dtype=f32, device=dev)
 
     def ops(self):
+        """The step: x and dY are each read once by the dual-orientation cast, which emits
+        both the row-wise operand (forward / dgrad) and the transposed one (wgrad)."""
+        fg = self.fg
+        return [
+            ("cast_x_dual", lambda: fg.cast_per_token_dual(self.x, self.xq, self.sx, self.xTq, self.sxT)),
+            ("cast_W", lambda: fg.cast_per_block(self.W, self.Wq, self.sW, self.WqT, self.sWT, fg.SF_FP32)),
+            ("gemm_fwd", lambda: fg.gemm_fp8_nt_bf16(self.xq, self.sx, self.Wq, self.sW, self.y)),
+            ("cast_dY_dual", lambda: fg.cast_per_token_dual(self.dY, self.dYq, self.sdY, self.dYTq, self.sdYT)),
+            ("gemm_dgrad", lambda: fg.gemm_fp8_nt_bf16(self.dYq, self.sdY, self.WqT, self.sWT, self.dX)),
+            ("gemm_wgrad", lambda: fg.wgrad_gemm_fp8_nt_fp32(self.dYTq, self.sdYT, self.xTq, self.sxT, self.dW)),
+        ]
+
+    def separate_cast_ops(self):
+        """The same four per-token casts as separate single-orientation launches (for reference)."""
         fg = self.fg
         return [
             ("cast_x", lambda: fg.cast_per_token(self.x, self.xq, self.sx, 128, fg.SF_FP32)),
-            ("cast_W", lambda: fg.cast_per_block(self.W, self.Wq, self.sW, self.WqT, self.sWT, fg.SF_FP32)),
-            ("gemm_fwd", lambda: fg.gemm_fp8_nt_bf16(self.xq, self.sx, self.Wq, self.sW, self.y)),
-            ("cast_dY", lambda: fg.cast_per_token(self.dY, self.dYq, self.sdY, 128, fg.SF_FP32)),
-            ("gemm_dgrad", lambda: fg.gemm_fp8_nt_bf16(self.dYq, self.sdY, self.WqT, self.sWT, self.dX)),
-            ("cast_dYT", lambda: fg.cast_per_token(self.dY.t(), self.dYTq, self.sdYT, 128, fg.SF_FP32)),
             ("cast_xT", lambda: fg.cast_per_token(self.x.t(), self.xTq, self.sxT, 128, fg.SF_FP32)),
-            ("gemm_wgrad", lambda: fg.wgrad_gemm_fp8_nt_fp32(self.dYTq, self.sdYT, self.xTq, self.sxT, self.dW)),
+            ("cast_dY", lambda: fg.cast_per_token(self.dY, self.dYq, self.sdY, 128, fg.SF_FP32)),
+            ("cast_dYT", lambda: fg.cast_per_token(self.dY.t(), self.dYTq, self.sdYT, 128, fg.SF_FP32)),
         ]
 
     def work(self):
@@ -86,11 +96,12 @@ class Linear:
         T, I, O = self.T, self.I, self.O
         f = 2.0 * T * I * O
         tok = lambda r, c: r * c * 2 + r * c + r * (c // 128) * 4
+        dual = lambda r, c: r * c * 2 + 2 * r * c + (r * (c // 128) + c * (r // 128)) * 4
         blk = O * I * 2 + 2 * O * I + 2 * (O // 128) * (I // 128) * 4
-        # GEMM bytes: A + B + scales + output (wgrad reads and writes fp32 D)
         return {
-            "cast_x": ("GB/s", tok(T, I)), "cast_W": ("GB/s", blk),
-            "cast_dY": ("GB/s", tok(T, O)), "cast_dYT": ("GB/s", tok(O, T)), "cast_xT": ("GB/s", tok(I, T)),
+            "cast_x_dual": ("GB/s", dual(T, I)), "cast_W": ("GB/s", blk), "cast_dY_dual": ("GB/s", dual(T, O)),
+            "cast_x": ("GB/s", tok(T, I)), "cast_xT": ("GB/s", tok(I, T)),
+            "cast_dY": ("GB/s", tok(T, O)), "cast_dYT": ("GB/s", tok(O, T)),
             "gemm_fwd": ("TFLOPS", f), "gemm_dgrad": ("TFLOPS", f), "gemm_wgrad": ("TFLOPS", f),
         }
 
@@ -343,7 +354,7 @@ def main():
         "dtype": "fp8_e4m3",
         "data": "synthetic",
         "config": {"workload": "fp8_linear_step tokens=8192 in=7168 out=4096 "
-                               "(casts + fwd + dgrad + wgrad GEMMs)",
+                               "(dual-orientation casts of x and dY, block cast of W, fwd + dgrad + wgrad GEMMs)",
                    "tokens": cfg["tokens"], "d_in": cfg["d_in"], "d_out": cfg["d_out"],
                    "gran_k": 128, "scales": "fp32", "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": dom_tflops, "peak": PEAK_FP8_TFLOPS,
@@ -354,6 +365,8 @@ def main():
     }
     if not args.no_extra:
         result["extra"] = extra_kernels(fg, torch, si)
+        result["extra"]["linear_step_separate_casts"] = {
+            name: _measure(torch, *work[name], fn) for name, fn in lin.separate_cast_ops()}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(si)
     print(json.dumps(result), flush=True)

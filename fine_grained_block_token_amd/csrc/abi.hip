@@ -101,6 +101,35 @@ int cast_per_block(const void *x, int x_dtype, int64_t rows, int64_t cols, int64
   return launched(fgfp8::launch_cast_per_block(a, static_cast<hipStream_t>(stream)));
 }
 
+// (r, g) -> r*s_row + g*s_grp is one of the two layouts the kernels write:
+// row-major (s_grp == 1, s_row >= groups) or MN-major (s_row == 1, s_grp >= rows).
+static bool scale_layout_ok(int64_t rows, int64_t groups, int64_t s_row, int64_t s_grp) {
+  return (s_grp == 1 && s_row >= groups) || (s_row == 1 && s_grp >= rows);
+}
+
+int cast_per_token_dual(const void *x, int x_dtype, int64_t rows, int64_t cols, int64_t x_ld, int sf_fmt,
+                        uint8_t *q, int64_t q_ld, void *sf, int64_t sf_stride_row, int64_t sf_stride_group,
+                        uint8_t *qT, int64_t qT_ld, void *sfT, int64_t sfT_stride_row,
+                        int64_t sfT_stride_group, void *stream) {
+  if (x_dtype != kInBf16) return FGFP8_EINVAL;
+  if (sf_fmt != kSfFp32 && sf_fmt != kSfUe8m0) return FGFP8_EINVAL;
+  if (rows < 0 || cols < 0) return FGFP8_EINVAL;
+  if (rows == 0 || cols == 0) return FGFP8_OK;
+  if (!x || !q || !sf || !qT || !sfT) return FGFP8_EINVAL;
+  if (!aligned(x, 16) || x_ld < cols || x_ld % 8 != 0) return FGFP8_EINVAL;
+  if (!aligned(q, 8) || q_ld < cols || q_ld % 8 != 0) return FGFP8_EINVAL;
+  if (!aligned(qT, 16) || qT_ld < rows || qT_ld % 16 != 0) return FGFP8_EINVAL;
+  if (!aligned(sf, 4) || !aligned(sfT, 4)) return FGFP8_EINVAL;
+  if (!scale_layout_ok(rows, cdiv(cols, 128), sf_stride_row, sf_stride_group)) return FGFP8_EINVAL;
+  if (!scale_layout_ok(cols, cdiv(rows, 128), sfT_stride_row, sfT_stride_group)) return FGFP8_EINVAL;
+  if (cdiv(rows, 128) * cdiv(cols, 128) > 0x7FFFFFFF) return FGFP8_EINVAL;
+  const int dev = check_device();
+  if (dev != FGFP8_OK) return dev;
+  fgfp8::CastDualArgs a{x, rows, cols, x_ld, sf_fmt, q, q_ld, sf, sf_stride_row, sf_stride_group,
+                        qT, qT_ld, sfT, sfT_stride_row, sfT_stride_group};
+  return launched(fgfp8::launch_cast_dual(a, static_cast<hipStream_t>(stream)));
+}
+
 static int check_gemm_common(const uint8_t *A, int64_t lda, const void *sa, int64_t sa_ld, const uint8_t *B,
                              int64_t ldb, const float *sb, const void *D, int64_t m, int64_t n, int64_t k) {
   if (m < 0 || n < 0 || k <= 0 || k % 128 != 0) return FGFP8_EINVAL;

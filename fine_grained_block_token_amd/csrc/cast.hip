@@ -413,6 +413,145 @@ __global__ __launch_bounds__(kThreads) void cast_block_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Dual-orientation per-token cast of a bf16 [rows, cols] matrix: the row-wise
+// cast (1x128 groups along cols) and the cast of its transpose (1x128 groups
+// along rows: the layout of the weight-gradient operands) from one read of x.
+// A 128x128 tile holds whole groups in both directions; one workgroup per tile.
+// Phase 1: lane (c = lane&15, j = lane>>4) of wave w loads columns [8c, 8c+8)
+// of tile rows 32w + 2(4i+j) + s (i < 4, s < 2) with 16-byte loads (4 rows of
+// 256 bytes per instruction); a 16-lane DPP max gives each row's amax and the
+// row's E4M3 bytes leave as 8-byte stores.  The bf16 pairs of rows (2v, 2v+1)
+// go to an LDS tile stored column-major (64 words per column) at word
+// v ^ 4h(col), h(f) = ((f>>3)^(f&3))&15, which keeps both the phase-1 dword
+// writes and the phase-2 16-byte reads free of bank conflicts.  Phase 2:
+// thread t owns columns t>>2 and 64+(t>>2), rows [32p, 32p+32) with p = t&3; a
+// 4-lane max gives each column group's amax and its E4M3 bytes leave as two
+// 16-byte stores.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int dual_word(int f, int v) { return f * 64 + (v ^ (4 * (((f >> 3) ^ (f & 3)) & 15))); }
+
+template <bool UE8M0>
+__global__ __launch_bounds__(kThreads) void cast_dual_kernel(
+    const uint16_t *__restrict__ x, int64_t rows, int64_t cols, int64_t ld, int64_t tiles_c,
+    uint8_t *__restrict__ q, int64_t q_ld, float *__restrict__ sf, int64_t sf_s_row, int64_t sf_s_grp,
+    uint8_t *__restrict__ qT, int64_t qT_ld, float *__restrict__ sfT, int64_t sfT_s_row, int64_t sfT_s_grp) {
+  __shared__ __attribute__((aligned(16))) uint32_t tile[128 * 64];
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int64_t r0 = (int64_t)(blockIdx.x / tiles_c) * 128, c0 = (int64_t)(blockIdx.x % tiles_c) * 128;
+  const int c = lane & 15, j = lane >> 4;
+  const int64_t fc = c0 + 8 * c;
+  const int validf = (int)max<int64_t>(0, min<int64_t>(8, cols - fc));
+
+  uint32_t raw[4][2][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int64_t r = r0 + 32 * wv + 2 * (4 * i + j) + s;
+      uint32_t w[4] = {0u, 0u, 0u, 0u};
+      if (r < rows && validf > 0) {
+        const uint16_t *p = x + r * ld + fc;
+        if (validf == 8) {
+          const uint4 v = *reinterpret_cast<const uint4 *>(p);
+          w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (e < validf) w[e >> 1] |= (uint32_t)p[e] << (16 * (e & 1));
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) raw[i][s][k] = w[k];
+    }
+
+  // rows: one 128-column group per tile row
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = (e & 1) ? bf16_hi(raw[i][s][e >> 1]) : bf16_lo(raw[i][s][e >> 1]);
+      uint32_t am = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) am = max(am, abs_bits(v[e]));
+      am = group_max_u32<16>(am);
+      const GroupScale gs = group_scale<UE8M0>(__uint_as_float(am));
+      const uint32_t w0 = e4m3x4(v[0] * gs.mult, v[1] * gs.mult, v[2] * gs.mult, v[3] * gs.mult);
+      const uint32_t w1 = e4m3x4(v[4] * gs.mult, v[5] * gs.mult, v[6] * gs.mult, v[7] * gs.mult);
+      const int64_t r = r0 + 32 * wv + 2 * (4 * i + j) + s;
+      if (r < rows) {
+        if (validf == 8) {
+          *reinterpret_cast<uint2 *>(q + r * q_ld + fc) = make_uint2(w0, w1);
+        } else if (validf > 0) {
+          uint8_t *qp = q + r * q_ld + fc;
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (e < validf) qp[e] = (uint8_t)((((e < 4) ? w0 : w1) >> (8 * (e & 3))) & 0xFFu);
+        }
+        if (c == 0) sf[r * sf_s_row + (c0 >> 7) * sf_s_grp] = gs.sf;
+      }
+    }
+
+  // transpose through LDS: word (col f, pair v) = bf16 of rows 2v (low) and 2v+1 (high)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int v = 16 * wv + 4 * i + j;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t lo = (raw[i][0][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+      const uint32_t hi = (raw[i][1][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+      tile[dual_word(8 * c + e, v)] = lo | (hi << 16);
+    }
+  }
+  __syncthreads();
+
+  // columns: one 128-row group per tile column
+  const int p = t & 3;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int fl = (t >> 2) + 64 * half;
+    uint32_t wd[16];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint4 a = *reinterpret_cast<const uint4 *>(&tile[dual_word(fl, 16 * p + 4 * k)]);
+      wd[4 * k] = a.x; wd[4 * k + 1] = a.y; wd[4 * k + 2] = a.z; wd[4 * k + 3] = a.w;
+    }
+    float v[32];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      v[2 * k] = bf16_lo(wd[k]);
+      v[2 * k + 1] = bf16_hi(wd[k]);
+    }
+    uint32_t am = 0;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) am = max(am, abs_bits(v[e]));
+    am = group_max_u32<4>(am);
+    const GroupScale gs = group_scale<UE8M0>(__uint_as_float(am));
+    uint32_t o[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+      o[m] = e4m3x4(v[4 * m] * gs.mult, v[4 * m + 1] * gs.mult, v[4 * m + 2] * gs.mult, v[4 * m + 3] * gs.mult);
+    const int64_t f = c0 + fl, tk = r0 + 32 * p;
+    if (f < cols) {
+      if (tk < rows) {
+        uint8_t *qp = qT + f * qT_ld + tk;
+        if (tk + 32 <= rows) {
+          reinterpret_cast<uint4 *>(qp)[0] = make_uint4(o[0], o[1], o[2], o[3]);
+          reinterpret_cast<uint4 *>(qp)[1] = make_uint4(o[4], o[5], o[6], o[7]);
+        } else {
+          const int valid = (int)(rows - tk);
+#pragma unroll
+          for (int e = 0; e < 32; ++e)
+            if (e < valid) qp[e] = (uint8_t)((o[e >> 2] >> (8 * (e & 3))) & 0xFFu);
+        }
+      }
+      if (p == 0) sfT[f * sfT_s_row + (r0 >> 7) * sfT_s_grp] = gs.sf;
+    }
+  }
+}
+
 template <typename TIn, int GRAN, int FMT>
 hipError_t launch_tok_rows(const void *x, int64_t rows, int64_t cols, int64_t xs_row, uint8_t *q,
                            int64_t q_ld, void *sf, int64_t sf_s_row, int64_t sf_s_grp, hipStream_t st) {
@@ -473,6 +612,22 @@ hipError_t launch_cast_per_token(const CastTokenArgs &a, hipStream_t st) {
                                   a.sf_stride_row, a.sf_stride_group, st);
   return dispatch_tok<float>(transposed, a.gran_k, a.sf_fmt, a.x, a.rows, a.cols, xs, a.q, a.q_ld, a.sf,
                              a.sf_stride_row, a.sf_stride_group, st);
+}
+
+hipError_t launch_cast_dual(const CastDualArgs &a, hipStream_t st) {
+  const int64_t tiles_c = (a.cols + 127) / 128, tiles = tiles_c * ((a.rows + 127) / 128);
+  const dim3 grid((unsigned)tiles);
+  const uint16_t *x = reinterpret_cast<const uint16_t *>(a.x);
+  float *sf = reinterpret_cast<float *>(a.sf), *sfT = reinterpret_cast<float *>(a.sfT);
+  if (a.sf_fmt == kSfUe8m0)
+    hipLaunchKernelGGL(cast_dual_kernel<true>, grid, dim3(kThreads), 0, st, x, a.rows, a.cols, a.x_ld, tiles_c,
+                       a.q, a.q_ld, sf, a.sf_stride_row, a.sf_stride_group, a.qT, a.qT_ld, sfT,
+                       a.sfT_stride_row, a.sfT_stride_group);
+  else
+    hipLaunchKernelGGL(cast_dual_kernel<false>, grid, dim3(kThreads), 0, st, x, a.rows, a.cols, a.x_ld, tiles_c,
+                       a.q, a.q_ld, sf, a.sf_stride_row, a.sf_stride_group, a.qT, a.qT_ld, sfT,
+                       a.sfT_stride_row, a.sfT_stride_group);
+  return hipGetLastError();
 }
 
 hipError_t launch_cast_per_block(const CastBlockArgs &a, hipStream_t st) {

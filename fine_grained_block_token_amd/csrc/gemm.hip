@@ -240,49 +240,46 @@ __global__ __launch_bounds__(C::kThreads, 2) void gemm_kernel(GemmArgs g, int ti
     p[i] = acc[i];
   }
 
-  // Pipeline (S = STAGES): step kb first waits until stage kb%S has landed (its
-  // own loads, then a bare s_barrier for everyone's), reads block kb's fragments
-  // and scales, issues the copy of block kb+S-1 into the stage read one step
-  // earlier, and runs block kb's MFMAs interleaved with the promotion of block
-  // kb-1.  The wait and the barrier sit at the top so that the fragment reads (and
-  // hence the MFMAs) cannot be scheduled above them; __syncthreads() is not used
-  // because its fence would also drain the prefetched stages.  Waves issue
-  // kLoads or kLoads + 1 loads per stage; waiting for at most kLoads outstanding
-  // loads (the one later stage, with three stages) guarantees the current stage
-  // has landed.
-  constexpr int kLoads = C::kALoads + C::kBLoads;
-  constexpr int S = C::kStages;
-  static_assert(S == 2 || S == 3, "two or three stages");
-#pragma unroll
-  for (int j = 0; j < S - 1; ++j)
-    if (j < KB) issue(j, smem + j * C::kStageBytes);
-
+  // Pipeline, two LDS stages; block kb lives in stage kb%2.  Step kb waits until
+  // its stage has landed (its own copies, then a bare s_barrier for everyone's,
+  // which also tells every wave that all reads of the other stage are done),
+  // issues the copy of block kb+1 into the other stage, reads block kb's
+  // fragments and scales and runs its MFMAs beside the promotion of block kb-1.
+  // The wait and the barrier are inline assembly so that the fragment reads
+  // cannot be scheduled above them; __syncthreads() is not used because its
+  // fence would also wait for the copy in flight.  (Measured on MI355X: issuing
+  // the copy of block kb+2 half-way through step kb behind a second barrier,
+  // or prefetching the next block into L2, does not help: the copy path's
+  // bytes per clock, not its latency, is the limit with 128x128 tiles.)
+  static_assert(C::kStages == 2, "two stages");
+  issue(0, smem);
   for (int kb = 0; kb < KB; ++kb) {
-    if (S == 3 && kb + 1 < KB) {
-      asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(kLoads) : "memory");
-    } else {
-      asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    }
-    const uint8_t *st = smem + (kb % S) * C::kStageBytes;
-    // all LDS reads of this stage precede the copy into the next free stage
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    const uint8_t *st = smem + (kb & 1) * C::kStageBytes;
+    // The copy into the free stage goes first: inline assembly bounds the
+    // scheduling region, and the fragment reads must share one with the MFMAs.
+    if (kb + 1 < KB) issue(kb + 1, smem + ((kb + 1) & 1) * C::kStageBytes);
     BlockScales cur;
     read_scales(kb, st, cur);
+    // Tiles run in a snake order (row 0 left to right, row 1 right to left, ...)
+    // so that each MFMA needs at most one fragment beyond the previous ones.
+    // Fragment read order: a0 b0 b1 | b2 | b3 | a1 | a2 | a3, each read at least two
+    // MFMAs ahead of its first use (b1 at 1, b2 at 2, b3 at 3, a1 at 4, a2 at 8,
+    // a3 at 12); sched_barrier pins this order (left alone, the scheduler hoists
+    // every read above the first MFMA, which then waits for all of them).
     v8i af[4], bf[4];
+    af[0] = frag(st, wm + (lane & 15), lane);
+    bf[0] = frag(st + C::kABytes, wn + (lane & 15), lane);
+    bf[1] = frag(st + C::kABytes, wn + 16 + (lane & 15), lane);
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi) af[mi] = frag(st, wm + 16 * mi + (lane & 15), lane);
-#pragma unroll
-    for (int ni = 0; ni < 4; ++ni) bf[ni] = frag(st + C::kABytes, wn + 16 * ni + (lane & 15), lane);
-    if (kb + S - 1 < KB) issue(kb + S - 1, smem + ((kb + S - 1) % S) * C::kStageBytes);
-    // promote block kb-1 (scales `prev`) while block kb's MFMAs run
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      promote<WGRAD>(acc[i], p[i], prev, i >> 2, i & 3);
-      p[i] = mfma_k128(bf[i & 3], af[i >> 2]);
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                 // 1 MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, WGRAD ? 8 : 4, 0);      // its share of VALU
+    for (int q = 0; q < 16; ++q) {
+      if (q < 2) bf[q + 2] = frag(st + C::kABytes, wn + 16 * (q + 2) + (lane & 15), lane);
+      else if (q < 5) af[q - 1] = frag(st, wm + 16 * (q - 1) + (lane & 15), lane);
+      const int mi = q >> 2, ni = (mi & 1) ? 3 - (q & 3) : (q & 3), i = 4 * mi + ni;
+      // promote tile i of block kb-1 (scales `prev`) beside block kb's MFMA
+      promote<WGRAD>(acc[i], p[i], prev, mi, ni);
+      p[i] = mfma_k128(bf[ni], af[mi]);
+      __builtin_amdgcn_sched_barrier(0);
     }
     prev = cur;
   }

@@ -36,6 +36,21 @@ struct CastBlockArgs {
   int64_t sfT_ld;
 };
 
+// Dual-orientation per-token cast (bf16 input, group 128, fp32 or UE8M0 scales).
+struct CastDualArgs {
+  const void *x;
+  int64_t rows, cols, x_ld;
+  int sf_fmt;
+  uint8_t *q;
+  int64_t q_ld;
+  void *sf;
+  int64_t sf_stride_row, sf_stride_group;
+  uint8_t *qT;
+  int64_t qT_ld;
+  void *sfT;
+  int64_t sfT_stride_row, sfT_stride_group;
+};
+
 // One GEMM problem.  wgrad == false: D bf16, sb one scale per 128x128 block
 // ((nb, kb) at sb[nb*sb_ld + kb]).  wgrad == true: D fp32 accumulated,
 // sb one scale per row and K block ((j, kb) at sb[kb*sb_ld + j]).
@@ -57,6 +72,7 @@ struct GemmArgs {
 
 hipError_t launch_cast_per_token(const CastTokenArgs &a, hipStream_t st);
 hipError_t launch_cast_per_block(const CastBlockArgs &a, hipStream_t st);
+hipError_t launch_cast_dual(const CastDualArgs &a, hipStream_t st);
 hipError_t launch_gemm(const GemmArgs &a, hipStream_t st);
 
 }  // namespace fgfp8

@@ -23,10 +23,10 @@ def declared_functions():
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
 
 
-def test_header_declares_the_four_calls():
+def test_header_declares_the_entry_points():
     names = declared_functions()
-    for f in ("cast_per_token", "cast_per_block", "gemm_fp8_nt_bf16", "wgrad_gemm_fp8_nt_fp32",
-              "fgfp8_status_string"):
+    for f in ("cast_per_token", "cast_per_block", "cast_per_token_dual", "gemm_fp8_nt_bf16",
+              "wgrad_gemm_fp8_nt_fp32", "fgfp8_status_string"):
         assert f in names
 
 
@@ -84,6 +84,29 @@ def blk(lib, **kw):
 ])
 def test_cast_per_block_rejects(lib, kw):
     assert blk(lib, **kw) == -1
+
+
+def dual(lib, **kw):
+    a = dict(x=P, dt=0, rows=256, cols=384, xld=384, fmt=0, q=Q, qld=384, sf=S, sfr=1, sfg=256,
+             qT=Q, qTld=256, sfT=S, sfTr=1, sfTg=384, st=None)
+    a.update(kw)
+    return lib.cast_per_token_dual(a["x"], a["dt"], a["rows"], a["cols"], a["xld"], a["fmt"], a["q"], a["qld"],
+                                   a["sf"], a["sfr"], a["sfg"], a["qT"], a["qTld"], a["sfT"], a["sfTr"],
+                                   a["sfTg"], a["st"])
+
+
+@pytest.mark.parametrize("kw", [
+    dict(dt=1), dict(fmt=2), dict(rows=-1), dict(x=None), dict(q=None), dict(sf=None), dict(qT=None),
+    dict(sfT=None), dict(xld=380), dict(xld=388), dict(x=ctypes.c_void_p(0x10008)), dict(qld=380),
+    dict(q=ctypes.c_void_p(0x20004)), dict(qTld=255), dict(qTld=264), dict(qT=ctypes.c_void_p(0x20008)),
+    dict(sfg=255), dict(sfr=2, sfg=1), dict(sfTg=383), dict(sfTr=1, sfTg=1), dict(sf=ctypes.c_void_p(0x30002)),
+])
+def test_cast_per_token_dual_rejects(lib, kw):
+    assert dual(lib, **kw) == -1
+
+
+def test_cast_per_token_dual_zero_size_is_ok(lib):
+    assert dual(lib, rows=0) == 0 and dual(lib, cols=0) == 0
 
 
 def gemm(lib, **kw):

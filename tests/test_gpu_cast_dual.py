@@ -1,0 +1,91 @@
+"""GPU parity of the dual-orientation per-token cast: one read of bf16 x gives
+q/sf bit-identical to the oracle's per-token cast of x and qT/sfT bit-identical
+to its per-token cast of x^T (1x128 groups; "DeepGEMM Essentials", Part 3, and
+the wgrad operands of "[Help] Starter script for nn.Linear for fwd,bwd").
+Writes must stay inside the given views."""
+import numpy as np
+import pytest
+import torch
+
+import fine_grained_block_token_amd as fg
+import oracle
+import synth_inputs as si
+from gpu_util import oracle_sf_bits, say, sentinel_u8
+
+pytestmark = pytest.mark.gpu
+
+
+def _scale_view(rows, groups, mn_major, pad):
+    """fp32 scale view [rows, groups] over a sentinel-filled buffer; returns (view, buffer)."""
+    if mn_major:
+        ld = -(-(rows + pad) // 4) * 4
+        buf = torch.full((groups, ld), -7, dtype=torch.int32, device="cuda")
+        return buf.view(torch.float32).t()[:rows], buf
+    buf = torch.full((rows, groups + pad), -7, dtype=torch.int32, device="cuda")
+    return buf.view(torch.float32)[:, :groups], buf
+
+
+def _run_dual(x_cpu, fmt, mn_major=True):
+    rows, cols = x_cpu.shape
+    x_ld = -(-cols // 8) * 8          # the kernel reads 16-byte chunks of each row
+    xbuf = torch.zeros((rows, x_ld), dtype=torch.bfloat16, device="cuda")
+    xbuf[:, :cols] = x_cpu.cuda()
+    x = xbuf[:, :cols]
+    q_ld = -(-(cols + 8) // 8) * 8
+    qT_ld = -(-(rows + 16) // 16) * 16
+    qbuf, qTbuf = sentinel_u8((rows, q_ld)), sentinel_u8((cols, qT_ld))
+    q, qT = qbuf[:, :cols], qTbuf[:, :rows]
+    G, GT = fg.num_groups(cols, 128), fg.num_groups(rows, 128)
+    sf, sbuf = _scale_view(rows, G, mn_major, 4)
+    sfT, sTbuf = _scale_view(cols, GT, mn_major, 4)
+    say("cast_per_token_dual", (rows, cols), "fmt", fmt, "mn", mn_major)
+    fg.cast_per_token_dual(x, q, sf, qT, sfT, fmt)
+    torch.cuda.synchronize()
+    got = (q.cpu().numpy(), sf.contiguous().view(torch.int32).cpu().numpy().view(np.uint32),
+           qT.cpu().numpy(), sfT.contiguous().view(torch.int32).cpu().numpy().view(np.uint32))
+    # nothing outside the views changed
+    assert (qbuf.cpu().numpy()[:, cols:] == 0xA5).all()
+    assert (qTbuf.cpu().numpy()[:, rows:] == 0xA5).all()
+    for buf, n, g in ((sbuf, rows, G), (sTbuf, cols, GT)):
+        b = buf.cpu().numpy()
+        assert ((b[:, n:] if mn_major else b[:, g:]) == -7).all()
+    return got
+
+
+def _check(x_cpu, fmt, mn_major=True):
+    q, sf, qT, sfT = _run_dual(x_cpu, fmt, mn_major)
+    oq, osf = oracle.cast_per_token(si.host_array(x_cpu), 128, fmt)
+    oqT, osfT = oracle.cast_per_token(si.host_array(x_cpu), 128, fmt, transpose=True)
+    assert np.array_equal(q, oq), "row-wise E4M3 bytes differ"
+    assert np.array_equal(sf, oracle_sf_bits(osf)), "row-wise scale bits differ"
+    assert np.array_equal(qT, oqT), "transposed E4M3 bytes differ"
+    assert np.array_equal(sfT, oracle_sf_bits(osfT)), "transposed scale bits differ"
+
+
+@pytest.mark.parametrize("shape", [(1, 512), (7, 4096), (129, 7168), (64, 1000), (128, 128), (129, 257),
+                                   (200, 300), (3000, 4096), (5, 3)])
+@pytest.mark.parametrize("fmt", [oracle.SF_FP32, oracle.SF_UE8M0], ids=["fp32", "ue8m0"])
+def test_dual_matches_both_casts(gpu, shape, fmt):
+    # the cast workloads carry an all-zero group and a group scaled by 1e4
+    _check(si.cast_workload(*shape, seed=si.SEED_A), fmt, mn_major=True)
+
+
+@pytest.mark.parametrize("shape", [(300, 200), (1000, 64)])
+def test_dual_row_major_scales(gpu, shape):
+    _check(si.cast_workload(*shape, seed=si.SEED_B), oracle.SF_FP32, mn_major=False)
+
+
+@pytest.mark.parametrize("shape", [(8192, 7168), (8192, 4096)], ids=["x", "dY"])
+def test_dual_linear_operands(gpu, shape):
+    # the linear step's x [tokens, in] and dY [tokens, out] at full size
+    _check(si.randn(shape, si.SEED_A if shape[1] == 7168 else si.SEED_DY), oracle.SF_FP32, mn_major=True)
+
+
+def test_dual_zero_size_is_noop(gpu):
+    x = torch.zeros((0, 256), dtype=torch.bfloat16, device="cuda")
+    q = torch.empty((0, 256), dtype=torch.uint8, device="cuda")
+    qT = torch.empty((256, 16), dtype=torch.uint8, device="cuda")[:, :0]
+    sf = fg.mn_major_scales(0, 2)
+    sfT = fg.mn_major_scales(256, 0)
+    fg.cast_per_token_dual(x, q, sf, qT, sfT)
+    torch.cuda.synchronize()
