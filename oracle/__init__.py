@@ -231,3 +231,39 @@ def wgrad_nt(A, sa, B, sb, d_in, idx=None):
     if idx is not None:
         d = d[idx[0], idx[1]]
     return d + ref, absum + np.abs(d)
+
+
+def m_grouped_gemm_nt(A, sa, B, sb, m_indices, idx=None):
+    """fp64 reference of the m-grouped contiguous GEMM ("DeepGEMM Essentials",
+    Parts 8-11): row i of A uses expert e = m_indices[i] and gives
+    D[i] = (A[i] * sa[i]) (B[e] * sb[e])^T; rows with m_indices[i] == -1 are
+    padding and have no reference (NaN).
+
+    A uint8 [m, k]; sa float32 [m, k/128]; B uint8 [E, n, k]; sb float32
+    [E, ceil(n/128), k/128]; m_indices int [m].  ``idx`` = (i_array, j_array)
+    computes only those outputs.  Returns (ref, absum) like gemm_nt.
+    """
+    A = np.asarray(A)
+    B = np.asarray(B)
+    sb = np.asarray(sb)
+    e_of = np.asarray(m_indices, dtype=np.int64)
+    m, n = A.shape[0], B.shape[1]
+    if idx is None:
+        ref = np.full((m, n), np.nan)
+        absum = np.full((m, n), np.nan)
+        for e in range(B.shape[0]):
+            rows = np.nonzero(e_of == e)[0]
+            if rows.size:
+                r, s = gemm_nt(A[rows], sa[rows], B[e], sb[e])
+                ref[rows], absum[rows] = r, s
+        return ref, absum
+    ii = np.asarray(idx[0], dtype=np.int64)
+    jj = np.asarray(idx[1], dtype=np.int64)
+    ref = np.full(ii.size, np.nan)
+    absum = np.full(ii.size, np.nan)
+    for e in range(B.shape[0]):
+        sel = np.nonzero(e_of[ii] == e)[0]
+        if sel.size:
+            r, s = gemm_nt(A, sa, B[e], sb[e], idx=(ii[sel], jj[sel]))
+            ref[sel], absum[sel] = r, s
+    return ref, absum

@@ -15,6 +15,7 @@ last 128-column group of the last row, which is also the partial group when
 """
 from __future__ import annotations
 
+import numpy as np
 import torch
 
 SEED_A, SEED_B, SEED_DY = 0, 1, 2
@@ -62,3 +63,20 @@ GEMM_SMALL = (128, 256, 512)                           # m, n, k
 GEMM_PREFILL = [(4096, 7168, 7168), (4096, 4096, 7168)]
 GEMM_DECODE = [(m, n, k) for m in (1, 64, 512) for (n, k) in ((7168, 4096), (4096, 7168))]
 LINEAR = dict(tokens=8192, d_in=7168, d_out=4096)
+
+
+def grouped_layout(tokens_per_expert, align: int = 128):
+    """m_indices of the contiguous grouped layout: expert e's tokens follow one another,
+    each expert's segment is padded to a multiple of ``align`` rows, padding rows are -1."""
+    parts = []
+    for e, t in enumerate(tokens_per_expert):
+        padded = -(-t // align) * align
+        parts.append(np.full(t, e, dtype=np.int32))
+        parts.append(np.full(padded - t, -1, dtype=np.int32))
+    return np.concatenate(parts) if parts else np.zeros(0, np.int32)
+
+
+# expert token counts of the grouped-GEMM walkthrough (4 experts) and of its
+# 8-expert exercise
+MOE_TOKENS_4 = [128, 96, 112, 144]
+MOE_TOKENS_8 = [64, 128, 96, 112, 88, 144, 72, 104]
