@@ -250,7 +250,34 @@ def extra_kernels(fg, torch, si):
         r["frac_hbm_peak"] = r["gbs"] / PEAK_HBM_GBS
         out[f"gemm_{m}x{n}x{k}"] = r
         del A, sa, B, sb, D, Bs
+    # m-grouped contiguous GEMM: the 8-expert token mix of the grouped-GEMM exercise
+    # (hidden 2048), as given and with 32x the tokens per expert
+    for scale in (1, 32):
+        tokens = [t * scale for t in si.MOE_TOKENS_8]
+        out[f"m_grouped_8experts_tokens{sum(tokens)}_hidden2048"] = grouped_gemm_rate(fg, torch, si, tokens, 2048, 2048)
     return out
+
+
+def grouped_gemm_rate(fg, torch, si, tokens, n, k):
+    """Per-launch time of the m-grouped GEMM on randn*0.1 operands; TFLOPS over the routed
+    (non-padding) rows, which is the useful work."""
+    import numpy as np
+    m_idx = torch.from_numpy(si.grouped_layout(tokens)).cuda()
+    m, E = m_idx.numel(), len(tokens)
+    a = si.randn((m, k), si.SEED_A, 0.1).cuda()
+    A = torch.empty((m, k), dtype=torch.uint8, device="cuda")
+    sa = fg.mn_major_scales(m, k // 128)
+    fg.cast_per_token(a, A, sa, 128, fg.SF_FP32)
+    B = torch.empty((E, n, k), dtype=torch.uint8, device="cuda")
+    sb = torch.empty((E, -(-n // 128), k // 128), dtype=torch.float32, device="cuda")
+    for e in range(E):
+        fg.cast_per_block(si.randn((n, k), si.SEED_B + e, 0.1).cuda(), B[e], sb[e], sf_fmt=fg.SF_FP32)
+    D = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    torch.cuda.synchronize()
+    r = _measure(torch, "TFLOPS", 2.0 * sum(tokens) * n * k,
+                 lambda: fg.m_grouped_gemm_fp8_nt_bf16_contiguous(A, sa, B, sb, m_idx, D))
+    r["rows_with_padding"] = m
+    return r
 
 
 def cpu_baseline(si, target_s=20.0):

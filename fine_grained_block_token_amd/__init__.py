@@ -44,8 +44,10 @@ def load():
     lib.cast_per_token_dual.argtypes = [p, i32, i64, i64, i64, i32, p, i64, p, i64, i64, p, i64, p, i64, i64, p]
     lib.gemm_fp8_nt_bf16.argtypes = [p, i64, p, i32, i64, p, i64, p, i64, p, i64, i64, i64, i64, p]
     lib.wgrad_gemm_fp8_nt_fp32.argtypes = [p, i64, p, i64, p, i64, p, i64, p, i64, i64, i64, i64, p]
+    lib.m_grouped_gemm_fp8_nt_bf16_contiguous.argtypes = [p, i64, p, i32, i64, p, i64, i64, p, i64, i64, p, i64,
+                                                          p, i64, i64, i64, i64, p]
     for f in ("cast_per_token", "cast_per_block", "cast_per_token_dual", "gemm_fp8_nt_bf16",
-              "wgrad_gemm_fp8_nt_fp32"):
+              "wgrad_gemm_fp8_nt_fp32", "m_grouped_gemm_fp8_nt_bf16_contiguous"):
         getattr(lib, f).restype = i32
     lib.fgfp8_status_string.argtypes = [i32]
     lib.fgfp8_status_string.restype = ctypes.c_char_p
@@ -54,7 +56,7 @@ def load():
 
 
 EXPORTED = ("cast_per_token", "cast_per_block", "cast_per_token_dual", "gemm_fp8_nt_bf16",
-            "wgrad_gemm_fp8_nt_fp32", "fgfp8_status_string")
+            "wgrad_gemm_fp8_nt_fp32", "m_grouped_gemm_fp8_nt_bf16_contiguous", "fgfp8_status_string")
 
 
 def _check(rc: int, what: str):
@@ -154,6 +156,25 @@ def gemm_fp8_nt_bf16(A: torch.Tensor, sa: torch.Tensor, B: torch.Tensor, sb: tor
     _check(load().gemm_fp8_nt_bf16(_ptr(A), A.stride(0), _ptr(sa), sa_fmt, sa_ld, _ptr(B), B.stride(0),
                                    _ptr(sb), sb.stride(0), _ptr(D), D.stride(0), m, n, k, _stream(A)),
            "gemm_fp8_nt_bf16")
+
+
+def m_grouped_gemm_fp8_nt_bf16_contiguous(A: torch.Tensor, sa: torch.Tensor, B: torch.Tensor, sb: torch.Tensor,
+                                          m_indices: torch.Tensor, D: torch.Tensor, sa_fmt: int = SF_FP32) -> None:
+    """MoE forward over a token-contiguous LHS: row i of D (bf16 [m, n]) = (A[i]*sa[i]) (B[e]*sb[e])^T with
+    e = m_indices[i] (int32, -1 = padding row, not written).  B: [E, n, k] E4M3; sb: [E, ceil(n/128), k/128]
+    float32; A, sa as gemm_fp8_nt_bf16."""
+    A, B = _u8(A), _u8(B)
+    m, k = A.shape
+    E, n = B.shape[0], B.shape[1]
+    if sa.shape[0] > 1 and sa.stride(0) != 1:
+        raise ValueError("sa must be MN-major (stride(0) == 1)")
+    if m_indices.dtype != torch.int32 or m_indices.numel() != m:
+        raise ValueError("m_indices must be int32 [m]")
+    sa_ld = sa.stride(1) if sa.dim() == 2 else m
+    _check(load().m_grouped_gemm_fp8_nt_bf16_contiguous(
+        _ptr(A), A.stride(0), _ptr(sa), sa_fmt, sa_ld, _ptr(B), B.stride(1), B.stride(0), _ptr(sb), sb.stride(1),
+        sb.stride(0), _ptr(m_indices), E, _ptr(D), D.stride(0), m, n, k, _stream(A)),
+        "m_grouped_gemm_fp8_nt_bf16_contiguous")
 
 
 def wgrad_gemm_fp8_nt_fp32(A: torch.Tensor, sa: torch.Tensor, B: torch.Tensor, sb: torch.Tensor,

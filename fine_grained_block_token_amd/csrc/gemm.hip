@@ -143,7 +143,7 @@ __device__ __forceinline__ void promote(v4f &acc, const v4f &p, const BlockScale
   }
 }
 
-template <class C, int SA_FMT, bool WGRAD>
+template <class C, int SA_FMT, bool WGRAD, bool GROUPED>
 __global__ __launch_bounds__(C::kThreads, 2) void gemm_kernel(GemmArgs g, int tiles_m, int tiles_n) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::kStages * C::kStageBytes];
   const int t = threadIdx.x, lane = t & 63;
@@ -164,6 +164,25 @@ __global__ __launch_bounds__(C::kThreads, 2) void gemm_kernel(GemmArgs g, int ti
   const int64_t m0 = (int64_t)tm * C::kBM, n0 = (int64_t)tn * C::kBN;
   const int64_t m = g.m, n = g.n;
   const int KB = (int)(g.k / kBK);
+
+  // m-grouped layout: the tile's 128 rows belong to one expert, the largest
+  // m_indices among them (-1 marks padding); a tile with no valid expert id
+  // writes nothing.  Every wave computes the same id, so the whole workgroup
+  // returns together, before any barrier.
+  const uint8_t *Bg = g.B;
+  const float *sbg = g.sb;
+  int expert = 0;
+  if constexpr (GROUPED) {
+    static_assert(C::kBM == 128, "one 128-row segment block per tile");
+    uint32_t v = 0;
+#pragma unroll
+    for (int r = 0; r < C::kBM; r += 64)
+      if (m0 + r + lane < m) v = max(v, (uint32_t)(g.m_idx[m0 + r + lane] + 1));
+    expert = (int)wave_max_u32(v) - 1;
+    if (expert < 0 || expert >= g.num_experts) return;
+    Bg = g.B + (int64_t)expert * g.b_estride;
+    sbg = g.sb + (int64_t)expert * g.sb_estride;
+  }
 
   // Direct-to-LDS copy of one stage (tiles and scales of one K block).  Offsets
   // are 32-bit from the tile's first row (the host bounds lda, ldb < 2^24).  Each 1 KB
@@ -190,7 +209,7 @@ __global__ __launch_bounds__(C::kThreads, 2) void gemm_kernel(GemmArgs g, int ti
                                        : 4u * (uint32_t)min((int64_t)(64 * (wv - C::kSaLoads) + lane), n - 1 - n0);
   auto issue = [&](int kb, uint8_t *st) {
     const uint8_t *ga = g.A + m0 * g.lda + (int64_t)kb * kBK;
-    const uint8_t *gb = g.B + n0 * g.ldb + (int64_t)kb * kBK;
+    const uint8_t *gb = Bg + n0 * g.ldb + (int64_t)kb * kBK;
 #pragma unroll
     for (int i = 0; i < C::kALoads; ++i) load_lds16(ga, a_off[i], st + 1024 * (i * C::kWaves + wv));
 #pragma unroll
@@ -203,7 +222,7 @@ __global__ __launch_bounds__(C::kThreads, 2) void gemm_kernel(GemmArgs g, int ti
       if constexpr (WGRAD) {
         load_lds4(g.sb + (int64_t)kb * g.sb_ld + n0, scale_off, st + C::kSbOff + 256 * (wv - C::kSaLoads));
       } else {   // forward: the tile's one block scale, the same dword in every lane
-        load_lds4(g.sb + (n0 >> 7) * g.sb_ld + kb, 0u, st + C::kSbOff + 256 * (wv - C::kSaLoads));
+        load_lds4(sbg + (n0 >> 7) * g.sb_ld + kb, 0u, st + C::kSbOff + 256 * (wv - C::kSaLoads));
       }
     }
   };
@@ -291,6 +310,9 @@ __global__ __launch_bounds__(C::kThreads, 2) void gemm_kernel(GemmArgs g, int ti
   for (int mi = 0; mi < 4; ++mi) {
     const int64_t i = m0 + wm + 16 * mi + (lane & 15);
     if (i >= m) continue;
+    if constexpr (GROUPED) {
+      if (g.m_idx[i] != expert) continue;   // padding (or another expert's) row
+    }
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni) {
       const int64_t j = n0 + wn + 16 * ni + 4 * (lane >> 4);
@@ -450,11 +472,18 @@ hipError_t launch_cfg(const GemmArgs &a, hipStream_t st) {
   const int per_xcd = (tiles + kXcds - 1) / kXcds;
   const dim3 grid((unsigned)(per_xcd * kXcds));
   if (a.wgrad) {
-    hipLaunchKernelGGL((gemm_kernel<C, kSfFp32, true>), grid, dim3(C::kThreads), 0, st, a, tiles_m, tiles_n);
+    hipLaunchKernelGGL((gemm_kernel<C, kSfFp32, true, false>), grid, dim3(C::kThreads), 0, st, a, tiles_m, tiles_n);
+  } else if (a.m_idx != nullptr) {
+    if (a.sa_fmt == kSfPackedUe8m0)
+      hipLaunchKernelGGL((gemm_kernel<C, kSfPackedUe8m0, false, true>), grid, dim3(C::kThreads), 0, st, a, tiles_m,
+                         tiles_n);
+    else
+      hipLaunchKernelGGL((gemm_kernel<C, kSfFp32, false, true>), grid, dim3(C::kThreads), 0, st, a, tiles_m, tiles_n);
   } else if (a.sa_fmt == kSfPackedUe8m0) {
-    hipLaunchKernelGGL((gemm_kernel<C, kSfPackedUe8m0, false>), grid, dim3(C::kThreads), 0, st, a, tiles_m, tiles_n);
+    hipLaunchKernelGGL((gemm_kernel<C, kSfPackedUe8m0, false, false>), grid, dim3(C::kThreads), 0, st, a, tiles_m,
+                       tiles_n);
   } else {
-    hipLaunchKernelGGL((gemm_kernel<C, kSfFp32, false>), grid, dim3(C::kThreads), 0, st, a, tiles_m, tiles_n);
+    hipLaunchKernelGGL((gemm_kernel<C, kSfFp32, false, false>), grid, dim3(C::kThreads), 0, st, a, tiles_m, tiles_n);
   }
   return hipGetLastError();
 }
@@ -473,7 +502,7 @@ hipError_t launch_skinny(const GemmArgs &a, hipStream_t st) {
 }
 
 hipError_t launch_gemm(const GemmArgs &a, hipStream_t st) {
-  if (!a.wgrad && a.m <= 64) {
+  if (!a.wgrad && a.m_idx == nullptr && a.m <= 64) {
     // decode-sized: stream B with K split over the waves of a workgroup
     if (a.m <= 16) return launch_skinny<1, 1, 8, 4>(a, st);
     if (a.m <= 32) return launch_skinny<2, 2, 8, 2>(a, st);

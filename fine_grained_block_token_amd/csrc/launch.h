@@ -68,6 +68,11 @@ struct GemmArgs {
   int64_t ldd;
   int64_t m, n, k;
   bool wgrad;
+  // m-grouped contiguous layout (forward only): row i uses expert m_idx[i]
+  // (-1 = padding, not written); expert e's B at B + e*b_estride and its
+  // scales at sb + e*sb_estride.  m_idx == nullptr: a plain GEMM.
+  const int32_t *m_idx = nullptr;
+  int64_t num_experts = 0, b_estride = 0, sb_estride = 0;
 };
 
 hipError_t launch_cast_per_token(const CastTokenArgs &a, hipStream_t st);

@@ -176,6 +176,38 @@ int gemm_fp8_nt_bf16(const uint8_t *A, int64_t lda, const void *sa, int sa_fmt, 
                      void *stream);
 
 /*
+ * m_grouped_gemm_fp8_nt_bf16_contiguous -- the forward GEMM of a mixture of
+ * experts over a token-contiguous LHS.  Defined by "DeepGEMM Essentials",
+ * Parts 8-11: the tokens routed to expert e are consecutive rows of A, each
+ * expert's run of rows is padded to a multiple of 128 (the contiguous-layout
+ * alignment), and m_indices[i] is the expert of row i, or -1 for a padding
+ * row.  Row i with m_indices[i] = e >= 0 gets
+ *     D[i, :] = (A[i] * sa[i]) (B_e * sb_e)^T,
+ * computed exactly as gemm_fp8_nt_bf16 computes a row; padding rows of D are
+ * not written.
+ *
+ * A, sa, sa_fmt, sa_ld, D, ldd, m, n, k   as gemm_fp8_nt_bf16 (m = all rows,
+ *          padding included).
+ * B        expert e's E4M3 [n, k] weights at B + e*b_expert_stride (bytes),
+ *          row-major with ldb; b_expert_stride >= (n-1)*ldb + k and a multiple
+ *          of 16.
+ * sb       expert e's fp32 [ceil(n/128), k/128] block scales at
+ *          sb + e*sb_expert_stride (floats), (nb, kb) at nb*sb_ld + kb.
+ * m_indices int32 [m], device memory; num_experts >= 1.
+ * Layout requirement (the contiguous layout above): every 128-row block
+ * [128t, 128t+128) of A holds rows of one expert and padding only.  A block
+ * is computed for the largest id among its rows; rows of any other expert in
+ * the block, rows with -1, and blocks whose id is not in [0, num_experts)
+ * are left unwritten (no memory outside the experts' weights is read).
+ */
+int m_grouped_gemm_fp8_nt_bf16_contiguous(const uint8_t *A, int64_t lda, const void *sa, int sa_fmt,
+                                          int64_t sa_ld, const uint8_t *B, int64_t ldb,
+                                          int64_t b_expert_stride, const float *sb, int64_t sb_ld,
+                                          int64_t sb_expert_stride, const int32_t *m_indices,
+                                          int64_t num_experts, uint16_t *D, int64_t ldd, int64_t m,
+                                          int64_t n, int64_t k, void *stream);
+
+/*
  * wgrad_gemm_fp8_nt_fp32 -- D += (A * sa)(B * sb)^T in fp32 (weight gradient).
  * Defined by "DeepGEMM Essentials", Parts 12-13 (the weight gradient is
  * accumulated into an existing fp32 tensor, expected = original + dY^T x)

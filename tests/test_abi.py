@@ -26,7 +26,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for f in ("cast_per_token", "cast_per_block", "cast_per_token_dual", "gemm_fp8_nt_bf16",
-              "wgrad_gemm_fp8_nt_fp32", "fgfp8_status_string"):
+              "wgrad_gemm_fp8_nt_fp32", "m_grouped_gemm_fp8_nt_bf16_contiguous", "fgfp8_status_string"):
         assert f in names
 
 
@@ -141,3 +141,25 @@ def wgrad(lib, **kw):
 @pytest.mark.parametrize("kw", [dict(sbld=100), dict(k=100), dict(ldd=254), dict(sb=None), dict(lda=1 << 24)])
 def test_wgrad_rejects(lib, kw):
     assert wgrad(lib, **kw) == -1
+
+
+def grouped(lib, **kw):
+    a = dict(A=P, lda=256, sa=S, fmt=0, sald=256, B=Q, ldb=256, bes=256 * 256, sb=S, sbld=2, sbes=4,
+             mi=S, E=4, D=P, ldd=256, m=256, n=256, k=256, st=None)
+    a.update(kw)
+    return lib.m_grouped_gemm_fp8_nt_bf16_contiguous(
+        a["A"], a["lda"], a["sa"], a["fmt"], a["sald"], a["B"], a["ldb"], a["bes"], a["sb"], a["sbld"], a["sbes"],
+        a["mi"], a["E"], a["D"], a["ldd"], a["m"], a["n"], a["k"], a["st"])
+
+
+@pytest.mark.parametrize("kw", [
+    dict(mi=None), dict(mi=ctypes.c_void_p(0x30002)), dict(E=0), dict(E=-1), dict(bes=255 * 256 + 200),
+    dict(bes=256 * 256 + 8), dict(sbes=3), dict(k=200), dict(sald=100), dict(fmt=7), dict(ldd=100),
+    dict(lda=1 << 24),
+])
+def test_m_grouped_rejects(lib, kw):
+    assert grouped(lib, **kw) == -1
+
+
+def test_m_grouped_zero_size_is_ok(lib):
+    assert grouped(lib, m=0) == 0 and grouped(lib, n=0) == 0
