@@ -258,6 +258,23 @@ def extra_kernels(fg, torch, si):
     return out
 
 
+def fused_output_cast(fg, torch, lin):
+    """The forward GEMM whose epilogue also emits the per-token FP8 cast of y (the next
+    layer's operand), against the forward GEMM followed by a separate cast of y."""
+    T, O = lin.T, lin.O
+    yq = torch.empty((T, O), dtype=torch.uint8, device="cuda")
+    ysf = fg.mn_major_scales(T, O // 128)
+    f = 2.0 * T * lin.I * O
+    fused = _measure(torch, "TFLOPS", f, lambda: fg.gemm_fp8_nt_bf16_cast(lin.xq, lin.sx, lin.Wq, lin.sW, lin.y,
+                                                                        yq, ysf))
+
+    def separate():
+        fg.gemm_fp8_nt_bf16(lin.xq, lin.sx, lin.Wq, lin.sW, lin.y)
+        fg.cast_per_token(lin.y, yq, ysf, 128, fg.SF_FP32)
+    return {"fused_ms": fused["ms"], "fused_tflops": fused["tflops"],
+            "gemm_then_cast_ms": _measure(torch, "TFLOPS", f, separate)["ms"]}
+
+
 def grouped_gemm_rate(fg, torch, si, tokens, n, k):
     """Per-launch time of the m-grouped GEMM on randn*0.1 operands; TFLOPS over the routed
     (non-padding) rows, which is the useful work."""
@@ -394,6 +411,7 @@ def main():
         result["extra"] = extra_kernels(fg, torch, si)
         result["extra"]["linear_step_separate_casts"] = {
             name: _measure(torch, *work[name], fn) for name, fn in lin.separate_cast_ops()}
+        result["extra"]["forward_with_output_cast"] = fused_output_cast(fg, torch, lin)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(si)
     print(json.dumps(result), flush=True)

@@ -44,10 +44,12 @@ def load():
     lib.cast_per_token_dual.argtypes = [p, i32, i64, i64, i64, i32, p, i64, p, i64, i64, p, i64, p, i64, i64, p]
     lib.gemm_fp8_nt_bf16.argtypes = [p, i64, p, i32, i64, p, i64, p, i64, p, i64, i64, i64, i64, p]
     lib.wgrad_gemm_fp8_nt_fp32.argtypes = [p, i64, p, i64, p, i64, p, i64, p, i64, i64, i64, i64, p]
+    lib.gemm_fp8_nt_bf16_cast.argtypes = [p, i64, p, i32, i64, p, i64, p, i64, p, i64, i32, p, i64, p, i64, i64,
+                                          i64, i64, i64, p]
     lib.m_grouped_gemm_fp8_nt_bf16_contiguous.argtypes = [p, i64, p, i32, i64, p, i64, i64, p, i64, i64, p, i64,
                                                           p, i64, i64, i64, i64, p]
     for f in ("cast_per_token", "cast_per_block", "cast_per_token_dual", "gemm_fp8_nt_bf16",
-              "wgrad_gemm_fp8_nt_fp32", "m_grouped_gemm_fp8_nt_bf16_contiguous"):
+              "wgrad_gemm_fp8_nt_fp32", "m_grouped_gemm_fp8_nt_bf16_contiguous", "gemm_fp8_nt_bf16_cast"):
         getattr(lib, f).restype = i32
     lib.fgfp8_status_string.argtypes = [i32]
     lib.fgfp8_status_string.restype = ctypes.c_char_p
@@ -56,7 +58,8 @@ def load():
 
 
 EXPORTED = ("cast_per_token", "cast_per_block", "cast_per_token_dual", "gemm_fp8_nt_bf16",
-            "wgrad_gemm_fp8_nt_fp32", "m_grouped_gemm_fp8_nt_bf16_contiguous", "fgfp8_status_string")
+            "wgrad_gemm_fp8_nt_fp32", "m_grouped_gemm_fp8_nt_bf16_contiguous", "gemm_fp8_nt_bf16_cast",
+            "fgfp8_status_string")
 
 
 def _check(rc: int, what: str):
@@ -156,6 +159,25 @@ def gemm_fp8_nt_bf16(A: torch.Tensor, sa: torch.Tensor, B: torch.Tensor, sb: tor
     _check(load().gemm_fp8_nt_bf16(_ptr(A), A.stride(0), _ptr(sa), sa_fmt, sa_ld, _ptr(B), B.stride(0),
                                    _ptr(sb), sb.stride(0), _ptr(D), D.stride(0), m, n, k, _stream(A)),
            "gemm_fp8_nt_bf16")
+
+
+def gemm_fp8_nt_bf16_cast(A: torch.Tensor, sa: torch.Tensor, B: torch.Tensor, sb: torch.Tensor,
+                          D: torch.Tensor | None, q: torch.Tensor, q_sf: torch.Tensor, sa_fmt: int = SF_FP32,
+                          q_sf_fmt: int = SF_FP32) -> None:
+    """gemm_fp8_nt_bf16 whose epilogue also emits the 1x128 per-token FP8 cast of the bf16 output:
+    ``q`` [m, n] E4M3 and ``q_sf`` [m, ceil(n/128)] float32 (row-major or MN-major view).  ``D`` may
+    be None to store only the FP8 output."""
+    A, B, q = _u8(A), _u8(B), _u8(q)
+    m, k = A.shape
+    n = B.shape[0]
+    if sa.shape[0] > 1 and sa.stride(0) != 1:
+        raise ValueError("sa must be MN-major (stride(0) == 1)")
+    sa_ld = sa.stride(1) if sa.dim() == 2 else m
+    _check(load().gemm_fp8_nt_bf16_cast(_ptr(A), A.stride(0), _ptr(sa), sa_fmt, sa_ld, _ptr(B), B.stride(0), _ptr(sb),
+                                        sb.stride(0), _ptr(D), 0 if D is None else D.stride(0), q_sf_fmt, _ptr(q),
+                                        q.stride(0), _ptr(q_sf), q_sf.stride(0), q_sf.stride(1), m, n, k,
+                                        _stream(A)),
+           "gemm_fp8_nt_bf16_cast")
 
 
 def m_grouped_gemm_fp8_nt_bf16_contiguous(A: torch.Tensor, sa: torch.Tensor, B: torch.Tensor, sb: torch.Tensor,

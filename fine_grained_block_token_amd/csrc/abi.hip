@@ -157,6 +157,32 @@ int gemm_fp8_nt_bf16(const uint8_t *A, int64_t lda, const void *sa, int sa_fmt, 
   return launched(fgfp8::launch_gemm(a, static_cast<hipStream_t>(stream)));
 }
 
+int gemm_fp8_nt_bf16_cast(const uint8_t *A, int64_t lda, const void *sa, int sa_fmt, int64_t sa_ld,
+                          const uint8_t *B, int64_t ldb, const float *sb, int64_t sb_ld, uint16_t *D, int64_t ldd,
+                          int q_sf_fmt, uint8_t *q, int64_t q_ld, float *q_sf, int64_t q_sf_stride_row,
+                          int64_t q_sf_stride_group, int64_t m, int64_t n, int64_t k, void *stream) {
+  if (sa_fmt != kSfFp32 && sa_fmt != kSfUe8m0 && sa_fmt != kSfPackedUe8m0) return FGFP8_EINVAL;
+  if (q_sf_fmt != kSfFp32 && q_sf_fmt != kSfUe8m0) return FGFP8_EINVAL;
+  // D is optional here: check_gemm_common wants a pointer, so hand it q
+  const int c = check_gemm_common(A, lda, sa, sa_ld, B, ldb, sb, q, m, n, k);
+  if (c != 1) return c;
+  if (sb_ld < k / 128) return FGFP8_EINVAL;
+  if (D && (!aligned(D, 16) || ldd < n || ldd % 8 != 0)) return FGFP8_EINVAL;
+  if (!aligned(q, 4) || q_ld < n || q_ld % 4 != 0) return FGFP8_EINVAL;
+  if (!q_sf || !aligned(q_sf, 4)) return FGFP8_EINVAL;
+  if (!scale_layout_ok(m, cdiv(n, 128), q_sf_stride_row, q_sf_stride_group)) return FGFP8_EINVAL;
+  const int dev = check_device();
+  if (dev != FGFP8_OK) return dev;
+  fgfp8::GemmArgs a{A, lda, sa, sa_fmt, sa_ld, B, ldb, sb, sb_ld, D, ldd, m, n, k, false};
+  a.q = q;
+  a.q_ld = q_ld;
+  a.cq_sf = q_sf;
+  a.cq_s_row = q_sf_stride_row;
+  a.cq_s_grp = q_sf_stride_group;
+  a.cq_fmt = q_sf_fmt;
+  return launched(fgfp8::launch_gemm(a, static_cast<hipStream_t>(stream)));
+}
+
 int m_grouped_gemm_fp8_nt_bf16_contiguous(const uint8_t *A, int64_t lda, const void *sa, int sa_fmt,
                                           int64_t sa_ld, const uint8_t *B, int64_t ldb, int64_t b_expert_stride,
                                           const float *sb, int64_t sb_ld, int64_t sb_expert_stride,

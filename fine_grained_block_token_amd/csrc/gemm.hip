@@ -143,7 +143,68 @@ __device__ __forceinline__ void promote(v4f &acc, const v4f &p, const BlockScale
   }
 }
 
-template <class C, int SA_FMT, bool WGRAD, bool GROUPED>
+// Per-token cast of the bf16 output fused into the epilogue: the 128 columns of a
+// tile row are exactly one 1x128 group ("DeepGEMM Essentials", Part 3: amax,
+// clamp, scale amax/448, E4M3), taken over the bf16-rounded values so that
+// the result equals casting the stored bf16 output.  A lane holds 16 of a
+// row's columns; the 4 lanes of that row in a wave (lane, lane^16, lane^32,
+// lane^48) reduce with shuffles, and the two waves holding the row's two
+// 64-column halves combine through LDS.
+template <class C, bool UE8M0>
+__device__ __forceinline__ void fused_cast_epilogue(const GemmArgs &g, const v4f (&acc)[16], int64_t m0, int64_t n0,
+                                                    int wm, int wn, int lane) {
+  static_assert(C::kBN == 128, "a tile row is one 128-column group");
+  __shared__ uint32_t half_amax[2][C::kBM];
+  const int64_t m = g.m, n = g.n;
+  uint32_t am[4];
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi) {
+    am[mi] = 0;
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) {
+      const int64_t j = n0 + wn + 16 * ni + 4 * (lane >> 4);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float v = __uint_as_float(bf16_rne(acc[4 * mi + ni][r]) << 16);
+        if (j + r < n) am[mi] = max(am[mi], __float_as_uint(v) & 0x7FFFFFFFu);
+      }
+    }
+    am[mi] = max(am[mi], (uint32_t)__shfl_xor((int)am[mi], 16));
+    am[mi] = max(am[mi], (uint32_t)__shfl_xor((int)am[mi], 32));
+  }
+  if (lane < 16) {
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) half_amax[wn >> 6][wm + 16 * mi + lane] = am[mi];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi) {
+    const int row = wm + 16 * mi + (lane & 15);
+    const int64_t i = m0 + row;
+    const GroupScale gs = group_scale<UE8M0>(__uint_as_float(max(half_amax[0][row], half_amax[1][row])));
+    if (i >= m) continue;
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) {
+      const int64_t j = n0 + wn + 16 * ni + 4 * (lane >> 4);
+      if (j >= n) continue;
+      float v[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[r] = __uint_as_float(bf16_rne(acc[4 * mi + ni][r]) << 16);
+      const uint32_t w = e4m3x4(v[0] * gs.mult, v[1] * gs.mult, v[2] * gs.mult, v[3] * gs.mult);
+      uint8_t *qp = g.q + i * g.q_ld + j;
+      if (j + 4 <= n) {
+        *reinterpret_cast<uint32_t *>(qp) = w;
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (j + r < n) qp[r] = (uint8_t)((w >> (8 * r)) & 0xFFu);
+      }
+    }
+    if (wn == 0 && (lane >> 4) == 0) g.cq_sf[i * g.cq_s_row + (n0 >> 7) * g.cq_s_grp] = gs.sf;
+  }
+}
+
+template <class C, int SA_FMT, bool WGRAD, bool GROUPED, int CASTF>
 __global__ __launch_bounds__(C::kThreads, 2) void gemm_kernel(GemmArgs g, int tiles_m, int tiles_n) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::kStages * C::kStageBytes];
   const int t = threadIdx.x, lane = t & 63;
@@ -306,12 +367,16 @@ __global__ __launch_bounds__(C::kThreads, 2) void gemm_kernel(GemmArgs g, int ti
   for (int i = 0; i < 16; ++i) promote<WGRAD>(acc[i], p[i], prev, i >> 2, i & 3);
 
   // epilogue: lane holds row i, columns j..j+3 of every 16x16 tile
+  if constexpr (CASTF != 0) fused_cast_epilogue<C, CASTF == 2>(g, acc, m0, n0, wm, wn, lane);
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi) {
     const int64_t i = m0 + wm + 16 * mi + (lane & 15);
     if (i >= m) continue;
     if constexpr (GROUPED) {
       if (g.m_idx[i] != expert) continue;   // padding (or another expert's) row
+    }
+    if constexpr (CASTF != 0) {
+      if (g.D == nullptr) continue;         // only the FP8 output was asked for
     }
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni) {
@@ -471,20 +536,23 @@ hipError_t launch_cfg(const GemmArgs &a, hipStream_t st) {
   const int tiles = tiles_m * tiles_n;
   const int per_xcd = (tiles + kXcds - 1) / kXcds;
   const dim3 grid((unsigned)(per_xcd * kXcds));
+#define FGFP8_GEMM(SAF, WG, GR, CF) \
+  hipLaunchKernelGGL((gemm_kernel<C, SAF, WG, GR, CF>), grid, dim3(C::kThreads), 0, st, a, tiles_m, tiles_n)
+  const bool packed = a.sa_fmt == kSfPackedUe8m0;
   if (a.wgrad) {
-    hipLaunchKernelGGL((gemm_kernel<C, kSfFp32, true, false>), grid, dim3(C::kThreads), 0, st, a, tiles_m, tiles_n);
+    FGFP8_GEMM(kSfFp32, true, false, 0);
   } else if (a.m_idx != nullptr) {
-    if (a.sa_fmt == kSfPackedUe8m0)
-      hipLaunchKernelGGL((gemm_kernel<C, kSfPackedUe8m0, false, true>), grid, dim3(C::kThreads), 0, st, a, tiles_m,
-                         tiles_n);
-    else
-      hipLaunchKernelGGL((gemm_kernel<C, kSfFp32, false, true>), grid, dim3(C::kThreads), 0, st, a, tiles_m, tiles_n);
-  } else if (a.sa_fmt == kSfPackedUe8m0) {
-    hipLaunchKernelGGL((gemm_kernel<C, kSfPackedUe8m0, false, false>), grid, dim3(C::kThreads), 0, st, a, tiles_m,
-                       tiles_n);
+    if (packed) FGFP8_GEMM(kSfPackedUe8m0, false, true, 0); else FGFP8_GEMM(kSfFp32, false, true, 0);
+  } else if (a.q != nullptr) {
+    if (a.cq_fmt == kSfUe8m0) {
+      if (packed) FGFP8_GEMM(kSfPackedUe8m0, false, false, 2); else FGFP8_GEMM(kSfFp32, false, false, 2);
+    } else {
+      if (packed) FGFP8_GEMM(kSfPackedUe8m0, false, false, 1); else FGFP8_GEMM(kSfFp32, false, false, 1);
+    }
   } else {
-    hipLaunchKernelGGL((gemm_kernel<C, kSfFp32, false, false>), grid, dim3(C::kThreads), 0, st, a, tiles_m, tiles_n);
+    if (packed) FGFP8_GEMM(kSfPackedUe8m0, false, false, 0); else FGFP8_GEMM(kSfFp32, false, false, 0);
   }
+#undef FGFP8_GEMM
   return hipGetLastError();
 }
 
@@ -502,7 +570,7 @@ hipError_t launch_skinny(const GemmArgs &a, hipStream_t st) {
 }
 
 hipError_t launch_gemm(const GemmArgs &a, hipStream_t st) {
-  if (!a.wgrad && a.m_idx == nullptr && a.m <= 64) {
+  if (!a.wgrad && a.m_idx == nullptr && a.q == nullptr && a.m <= 64) {
     // decode-sized: stream B with K split over the waves of a workgroup
     if (a.m <= 16) return launch_skinny<1, 1, 8, 4>(a, st);
     if (a.m <= 32) return launch_skinny<2, 2, 8, 2>(a, st);

@@ -73,6 +73,15 @@ struct GemmArgs {
   // scales at sb + e*sb_estride.  m_idx == nullptr: a plain GEMM.
   const int32_t *m_idx = nullptr;
   int64_t num_experts = 0, b_estride = 0, sb_estride = 0;
+  // Per-token cast of the bf16 output fused into the epilogue (forward only):
+  // q [m, n] E4M3 (q_ld) and one scale per row and 128-column group at
+  // cq_sf[i*cq_s_row + g*cq_s_grp]; cq_fmt kSfFp32 or kSfUe8m0.  D may then be
+  // nullptr (the bf16 output is not stored).  q == nullptr: no fused cast.
+  uint8_t *q = nullptr;
+  int64_t q_ld = 0;
+  float *cq_sf = nullptr;
+  int64_t cq_s_row = 0, cq_s_grp = 0;
+  int cq_fmt = 0;
 };
 
 hipError_t launch_cast_per_token(const CastTokenArgs &a, hipStream_t st);

@@ -176,6 +176,31 @@ int gemm_fp8_nt_bf16(const uint8_t *A, int64_t lda, const void *sa, int sa_fmt, 
                      void *stream);
 
 /*
+ * gemm_fp8_nt_bf16_cast -- gemm_fp8_nt_bf16 with the per-token FP8 cast of its
+ * output fused into the epilogue, so that the next layer's FP8 operand leaves
+ * the GEMM directly ("[Help] Starter script for nn.Linear for fwd,bwd": the
+ * maintainers' advice to fuse as much as possible; the cast is "DeepGEMM
+ * Essentials", Part 3, with 1 x 128 groups along n).
+ *
+ * A, sa, sa_fmt, sa_ld, B, ldb, sb, sb_ld, m, n, k   as gemm_fp8_nt_bf16.
+ * D, ldd      the bf16 output as gemm_fp8_nt_bf16, or D == NULL to store only
+ *             the FP8 output.
+ * q, q_ld     E4M3 [m, n]: q_ld >= n, multiple of 4; q 4-byte aligned.
+ * q_sf        fp32 scale of row i, 128-column group g at
+ *             q_sf[i*q_sf_stride_row + g*q_sf_stride_group], g < ceil(n/128);
+ *             row-major or MN-major as for cast_per_token.
+ * q_sf_fmt    FGFP8_SF_FP32 or FGFP8_SF_UE8M0.
+ * (q, q_sf) are bit-identical to cast_per_token(D, gran_k = 128, q_sf_fmt)
+ * applied to the bf16 output D of the same call.
+ */
+int gemm_fp8_nt_bf16_cast(const uint8_t *A, int64_t lda, const void *sa, int sa_fmt, int64_t sa_ld,
+                          const uint8_t *B, int64_t ldb, const float *sb, int64_t sb_ld,
+                          uint16_t *D, int64_t ldd,
+                          int q_sf_fmt, uint8_t *q, int64_t q_ld,
+                          float *q_sf, int64_t q_sf_stride_row, int64_t q_sf_stride_group,
+                          int64_t m, int64_t n, int64_t k, void *stream);
+
+/*
  * m_grouped_gemm_fp8_nt_bf16_contiguous -- the forward GEMM of a mixture of
  * experts over a token-contiguous LHS.  Defined by "DeepGEMM Essentials",
  * Parts 8-11: the tokens routed to expert e are consecutive rows of A, each

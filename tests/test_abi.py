@@ -26,7 +26,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for f in ("cast_per_token", "cast_per_block", "cast_per_token_dual", "gemm_fp8_nt_bf16",
-              "wgrad_gemm_fp8_nt_fp32", "m_grouped_gemm_fp8_nt_bf16_contiguous", "fgfp8_status_string"):
+              "wgrad_gemm_fp8_nt_fp32", "m_grouped_gemm_fp8_nt_bf16_contiguous", "gemm_fp8_nt_bf16_cast",
+              "fgfp8_status_string"):
         assert f in names
 
 
@@ -163,3 +164,24 @@ def test_m_grouped_rejects(lib, kw):
 
 def test_m_grouped_zero_size_is_ok(lib):
     assert grouped(lib, m=0) == 0 and grouped(lib, n=0) == 0
+
+
+def gcast(lib, **kw):
+    a = dict(A=P, lda=256, sa=S, fmt=0, sald=128, B=Q, ldb=256, sb=S, sbld=2, D=P, ldd=256, qfmt=0, q=Q, qld=256,
+             qsf=S, qsr=1, qsg=128, m=128, n=256, k=256, st=None)
+    a.update(kw)
+    return lib.gemm_fp8_nt_bf16_cast(a["A"], a["lda"], a["sa"], a["fmt"], a["sald"], a["B"], a["ldb"], a["sb"],
+                                     a["sbld"], a["D"], a["ldd"], a["qfmt"], a["q"], a["qld"], a["qsf"], a["qsr"],
+                                     a["qsg"], a["m"], a["n"], a["k"], a["st"])
+
+
+@pytest.mark.parametrize("kw", [
+    dict(qfmt=2), dict(q=None), dict(qsf=None), dict(qld=250), dict(qld=258), dict(q=ctypes.c_void_p(0x20002)),
+    dict(qsr=1, qsg=100), dict(qsr=1, qsg=1), dict(ldd=100), dict(D=ctypes.c_void_p(0x10004)), dict(k=200),
+])
+def test_gemm_cast_rejects(lib, kw):
+    assert gcast(lib, **kw) == -1
+
+
+def test_gemm_cast_zero_size_is_ok(lib):
+    assert gcast(lib, m=0) == 0 and gcast(lib, n=0) == 0
