@@ -267,3 +267,29 @@ def m_grouped_gemm_nt(A, sa, B, sb, m_indices, idx=None):
             r, s = gemm_nt(A, sa, B[e], sb[e], idx=(ii[sel], jj[sel]))
             ref[sel], absum[sel] = r, s
     return ref, absum
+
+
+def gemm_nt_g32(A, sa, B, sb, idx=None):
+    """fp64 reference of the NT GEMM with one scale per row and 32-wide K group on both
+    operands (the UE8M0 group-32 recipe named in "deep-gemm: fused per-token FP8 cast
+    in Triton"): D[i, j] = sum_g sa[i, g] sb[j, g] sum_{t in g} A[i, t] B[j, t].
+
+    A uint8 E4M3 [m, k]; sa float32 [m, k/32]; B uint8 E4M3 [n, k]; sb float32
+    [n, k/32] (the scales as values, e.g. unpack_ue8m0 of the packed words).  The
+    dequantised operands are exact in fp64 (E4M3 values times powers of two); the sum
+    uses a library fp64 matrix product.  ``idx`` = (i_array, j_array) computes only
+    those outputs.  Returns (ref, absum) like gemm_nt.
+    """
+    A = np.ascontiguousarray(A, dtype=np.uint8)
+    B = np.ascontiguousarray(B, dtype=np.uint8)
+    m, k = A.shape
+    n = B.shape[0]
+    if B.shape[1] != k or k % 32 or np.shape(sa) != (m, k // 32) or np.shape(sb) != (n, k // 32):
+        raise ValueError("bad group-32 GEMM shapes")
+    a = e4m3_value(A).astype(np.float64) * np.repeat(np.asarray(sa, np.float64), 32, axis=1)
+    b = e4m3_value(B).astype(np.float64) * np.repeat(np.asarray(sb, np.float64), 32, axis=1)
+    if idx is None:
+        return a @ b.T, np.abs(a) @ np.abs(b).T
+    ii = np.asarray(idx[0], dtype=np.int64)
+    jj = np.asarray(idx[1], dtype=np.int64)
+    return np.einsum("ij,ij->i", a[ii], b[jj]), np.einsum("ij,ij->i", np.abs(a[ii]), np.abs(b[jj]))

@@ -1,0 +1,61 @@
+"""Pins for the oracle's group-32 GEMM (both operands scaled per row and 32-wide
+K group; the UE8M0 group-32 recipe of "deep-gemm: fused per-token FP8 cast in
+Triton").  Independent pins: a per-element loop over PyTorch's float8 decoder
+on a tiny shape; equality with the 128-block oracle (the C implementation)
+when the four 32-groups of every 128-block share one scale; an all-ones closed
+form; the packed-UE8M0 cast round trip."""
+import numpy as np
+import torch
+
+import oracle
+import synth_inputs as si
+
+
+def _dec(codes):
+    return torch.from_numpy(np.ascontiguousarray(codes)).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def _g32_operands(m, n, k, seed):
+    qa, wa = oracle.cast_per_token(si.host_array(si.randn((m, k), seed)), 32, oracle.SF_PACKED_UE8M0)
+    qb, wb = oracle.cast_per_token(si.host_array(si.randn((n, k), seed + 1)), 32, oracle.SF_PACKED_UE8M0)
+    return qa, oracle.unpack_ue8m0(wa, k // 32), qb, oracle.unpack_ue8m0(wb, k // 32)
+
+
+def test_loop_brute_force():
+    qa, sa, qb, sb = _g32_operands(3, 5, 128, seed=4)
+    ref, absum = oracle.gemm_nt_g32(qa, sa, qb, sb)
+    a, b = _dec(qa), _dec(qb)
+    for i in range(3):
+        for j in range(5):
+            want = sum(float(sa[i, t // 32]) * float(sb[j, t // 32]) * a[i, t] * b[j, t] for t in range(128))
+            assert ref[i, j] == want or abs(ref[i, j] - want) <= 1e-15 * absum[i, j]
+
+
+def test_equals_block_oracle_when_groups_share_a_scale():
+    m, n, k = 40, 70, 512
+    qa, sa, qb, sb = _g32_operands(m, n, k, seed=8)
+    sa128 = sa[:, ::4].copy()
+    sb128 = sb[:, ::4].copy()
+    ref, _ = oracle.gemm_nt_g32(qa, np.repeat(sa128, 4, axis=1), qb, np.repeat(sb128, 4, axis=1))
+    want, _ = oracle.gemm_nt(qa, sa128, qb, sb128, sb_block=False)
+    assert np.allclose(ref, want, rtol=1e-14, atol=0)
+
+
+def test_all_ones_closed_form():
+    m, n, k = 4, 6, 256
+    rng = np.random.default_rng(0)
+    ea = rng.integers(-3, 4, (m, k // 32))
+    eb = rng.integers(-3, 4, (n, k // 32))
+    ref, _ = oracle.gemm_nt_g32(np.full((m, k), 0x38, np.uint8), np.ldexp(1.0, ea).astype(np.float32),
+                                np.full((n, k), 0x38, np.uint8), np.ldexp(1.0, eb).astype(np.float32))
+    want = np.array([[sum(32 * 2.0 ** (ea[i, g] + eb[j, g]) for g in range(k // 32)) for j in range(n)]
+                     for i in range(m)])
+    assert np.array_equal(ref, want)
+
+
+def test_sampled_equals_full():
+    qa, sa, qb, sb = _g32_operands(33, 65, 256, seed=12)
+    ref, absum = oracle.gemm_nt_g32(qa, sa, qb, sb)
+    ii, jj = np.array([0, 32, 5, 17]), np.array([64, 0, 33, 1])
+    r, a = oracle.gemm_nt_g32(qa, sa, qb, sb, idx=(ii, jj))
+    assert np.allclose(r, ref[ii, jj], rtol=1e-15, atol=1e-300) and np.allclose(a, absum[ii, jj], rtol=1e-15)
