@@ -250,6 +250,22 @@ def extra_kernels(fg, torch, si):
         r["frac_hbm_peak"] = r["gbs"] / PEAK_HBM_GBS
         out[f"gemm_{m}x{n}x{k}"] = r
         del A, sa, B, sb, D, Bs
+    # UE8M0 group-32 recipe (both operands scaled per row and 32-wide K group, applied by the
+    # scaled MFMA: no promotion) at the prefill and linear-forward shapes
+    for (m, n, k) in ((4096, 7168, 7168), (8192, 4096, 7168)):
+        a = si.randn((m, k), si.SEED_A, 0.1).cuda()
+        b = si.randn((n, k), si.SEED_B, 0.1).cuda()
+        A = torch.empty((m, k), dtype=torch.uint8, device="cuda")
+        B = torch.empty((n, k), dtype=torch.uint8, device="cuda")
+        wa = fg.mn_major_scales(m, k // 128, torch.int32)
+        wb = fg.mn_major_scales(n, k // 128, torch.int32)
+        fg.cast_per_token(a, A, wa, 32, fg.SF_PACKED_UE8M0)
+        fg.cast_per_token(b, B, wb, 32, fg.SF_PACKED_UE8M0)
+        D = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+        torch.cuda.synchronize()
+        out[f"gemm_ue8m0_g32_{m}x{n}x{k}"] = _measure(torch, "TFLOPS", 2.0 * m * n * k,
+                                                      lambda: fg.gemm_fp8_nt_bf16_ue8m0_g32(A, wa, B, wb, D))
+        del a, b, A, B, wa, wb, D
     # m-grouped contiguous GEMM: the 8-expert token mix of the grouped-GEMM exercise
     # (hidden 2048), as given and with 32x the tokens per expert
     for scale in (1, 32):

@@ -46,10 +46,12 @@ def load():
     lib.wgrad_gemm_fp8_nt_fp32.argtypes = [p, i64, p, i64, p, i64, p, i64, p, i64, i64, i64, i64, p]
     lib.gemm_fp8_nt_bf16_cast.argtypes = [p, i64, p, i32, i64, p, i64, p, i64, p, i64, i32, p, i64, p, i64, i64,
                                           i64, i64, i64, p]
+    lib.gemm_fp8_nt_bf16_ue8m0_g32.argtypes = [p, i64, p, i64, p, i64, p, i64, p, i64, i64, i64, i64, p]
     lib.m_grouped_gemm_fp8_nt_bf16_contiguous.argtypes = [p, i64, p, i32, i64, p, i64, i64, p, i64, i64, p, i64,
                                                           p, i64, i64, i64, i64, p]
     for f in ("cast_per_token", "cast_per_block", "cast_per_token_dual", "gemm_fp8_nt_bf16",
-              "wgrad_gemm_fp8_nt_fp32", "m_grouped_gemm_fp8_nt_bf16_contiguous", "gemm_fp8_nt_bf16_cast"):
+              "wgrad_gemm_fp8_nt_fp32", "m_grouped_gemm_fp8_nt_bf16_contiguous", "gemm_fp8_nt_bf16_cast",
+              "gemm_fp8_nt_bf16_ue8m0_g32"):
         getattr(lib, f).restype = i32
     lib.fgfp8_status_string.argtypes = [i32]
     lib.fgfp8_status_string.restype = ctypes.c_char_p
@@ -59,7 +61,7 @@ def load():
 
 EXPORTED = ("cast_per_token", "cast_per_block", "cast_per_token_dual", "gemm_fp8_nt_bf16",
             "wgrad_gemm_fp8_nt_fp32", "m_grouped_gemm_fp8_nt_bf16_contiguous", "gemm_fp8_nt_bf16_cast",
-            "fgfp8_status_string")
+            "gemm_fp8_nt_bf16_ue8m0_g32", "fgfp8_status_string")
 
 
 def _check(rc: int, what: str):
@@ -178,6 +180,24 @@ def gemm_fp8_nt_bf16_cast(A: torch.Tensor, sa: torch.Tensor, B: torch.Tensor, sb
                                         q.stride(0), _ptr(q_sf), q_sf.stride(0), q_sf.stride(1), m, n, k,
                                         _stream(A)),
            "gemm_fp8_nt_bf16_cast")
+
+
+def gemm_fp8_nt_bf16_ue8m0_g32(A: torch.Tensor, sa: torch.Tensor, B: torch.Tensor, sb: torch.Tensor,
+                               D: torch.Tensor) -> None:
+    """D[m, n] (bf16) = (A*sa)(B*sb)^T with one power-of-two scale per row and 32-wide K group on both
+    operands: sa [m, k/128] and sb [n, k/128] int32 packed-UE8M0 words in MN-major views (what
+    cast_per_token(gran_k=32, SF_PACKED_UE8M0) writes into mn_major_scales(..., torch.int32))."""
+    A, B = _u8(A), _u8(B)
+    m, k = A.shape
+    n = B.shape[0]
+    for s_ in (sa, sb):
+        if s_.shape[0] > 1 and s_.stride(0) != 1:
+            raise ValueError("scales must be MN-major (stride(0) == 1)")
+    sa_ld = sa.stride(1) if sa.dim() == 2 else m
+    sb_ld = sb.stride(1) if sb.dim() == 2 else n
+    _check(load().gemm_fp8_nt_bf16_ue8m0_g32(_ptr(A), A.stride(0), _ptr(sa), sa_ld, _ptr(B), B.stride(0), _ptr(sb),
+                                             sb_ld, _ptr(D), D.stride(0), m, n, k, _stream(A)),
+           "gemm_fp8_nt_bf16_ue8m0_g32")
 
 
 def m_grouped_gemm_fp8_nt_bf16_contiguous(A: torch.Tensor, sa: torch.Tensor, B: torch.Tensor, sb: torch.Tensor,

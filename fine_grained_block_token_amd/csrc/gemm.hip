@@ -409,6 +409,133 @@ __global__ __launch_bounds__(C::kThreads, 2) void gemm_kernel(GemmArgs g, int ti
   }
 }
 
+// UE8M0 group-32 recipe: both operands carry one power-of-two scale per row and
+// 32-wide K group (packed as in "deep-gemm: fused per-token FP8 cast in Triton":
+// the word of 128-K block kb holds the exponent bytes e+127 of its four groups).
+// V_MFMA_SCALE_F32_16X16X128_F8F6F4 takes one E8M0 scale per lane, and (measured
+// on MI355X) the scale of lane l covers row l&15 in register half (l>>5) (v0-3
+// or v4-7) of lane groups 2((l>>4)&1) and 2((l>>4)&1)+1.  Loading a lane of group
+// G = l>>4 with the row's 16-byte chunks G (into v0-3) and G+4 (into v4-7) --
+// the same K order for both operands -- puts 32-K group G of the block exactly
+// under the scale of lanes 16G..16G+15, which is byte G of the packed word.  The
+// scaling then happens inside the MFMA, which accumulates straight into the
+// fp32 accumulator: no promotion.  Each register half holds 16 consecutive
+// K bytes, so the MFMA's runs of 8 products are still 8 consecutive K.  Tiles,
+// copies, waits and fragment order are those of gemm_kernel.
+__device__ __forceinline__ v8i frag_g32(const uint8_t *tile, int row, int lane) {
+  const int c = lane >> 4;
+  const u32x4 lo = *reinterpret_cast<const u32x4 *>(tile + swz(row, c));
+  const u32x4 hi = *reinterpret_cast<const u32x4 *>(tile + swz(row, c + 4));
+  v8i r;
+  r[0] = (int)lo[0]; r[1] = (int)lo[1]; r[2] = (int)lo[2]; r[3] = (int)lo[3];
+  r[4] = (int)hi[0]; r[5] = (int)hi[1]; r[6] = (int)hi[2]; r[7] = (int)hi[3];
+  return r;
+}
+
+template <class C>
+__global__ __launch_bounds__(C::kThreads, 2) void gemm_g32_kernel(GemmArgs g, int tiles_m, int tiles_n) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::kStages * C::kStageBytes];
+  const int t = threadIdx.x, lane = t & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wm = (wv / C::WAVES_N_) * 64, wn = (wv % C::WAVES_N_) * 64;
+  const int tiles = tiles_m * tiles_n;
+  const int per_xcd = (tiles + kXcds - 1) / kXcds;
+  const int tid = (int)(blockIdx.x % kXcds) * per_xcd + (int)(blockIdx.x / kXcds);
+  if (tid >= tiles) return;
+  const int band = tid / (kGroupM * tiles_n);
+  const int band_m = min(kGroupM, tiles_m - band * kGroupM);
+  const int in_band = tid - band * kGroupM * tiles_n;
+  const int tm = band * kGroupM + in_band % band_m;
+  const int tn = in_band / band_m;
+  const int64_t m0 = (int64_t)tm * C::kBM, n0 = (int64_t)tn * C::kBN;
+  const int64_t m = g.m, n = g.n;
+  const int KB = (int)(g.k / kBK);
+
+  uint32_t a_off[C::kALoads], b_off[C::kBLoads];
+#pragma unroll
+  for (int i = 0; i < C::kALoads; ++i) {
+    const int s = 64 * (i * C::kWaves + wv) + lane, row = s >> 3, chunk = (s & 7) ^ swz_key(row);
+    a_off[i] = (uint32_t)(min((int64_t)row, m - 1 - m0) * g.lda) + (uint32_t)(chunk * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < C::kBLoads; ++i) {
+    const int s = 64 * (i * C::kWaves + wv) + lane, row = s >> 3, chunk = (s & 7) ^ swz_key(row);
+    b_off[i] = (uint32_t)(min((int64_t)row, n - 1 - n0) * g.ldb) + (uint32_t)(chunk * 16);
+  }
+  // scale words of block kb: the tile's rows (A) then its columns (B), 64 per wave
+  static_assert(C::kSaLoads + C::kSbLoads <= C::kWaves, "one scale load per wave at most");
+  const bool sa_loader = wv < C::kSaLoads;
+  const bool sb_loader = wv >= C::kSaLoads && wv < C::kSaLoads + C::kSbLoads;
+  const uint32_t scale_off = sa_loader ? 4u * (uint32_t)min((int64_t)(64 * wv + lane), m - 1 - m0)
+                                       : 4u * (uint32_t)min((int64_t)(64 * (wv - C::kSaLoads) + lane), n - 1 - n0);
+  const uint32_t *saw = reinterpret_cast<const uint32_t *>(g.sa);
+  const uint32_t *sbw = reinterpret_cast<const uint32_t *>(g.sb);
+  auto issue = [&](int kb, uint8_t *st) {
+    const uint8_t *ga = g.A + m0 * g.lda + (int64_t)kb * kBK;
+    const uint8_t *gb = g.B + n0 * g.ldb + (int64_t)kb * kBK;
+#pragma unroll
+    for (int i = 0; i < C::kALoads; ++i) load_lds16(ga, a_off[i], st + 1024 * (i * C::kWaves + wv));
+#pragma unroll
+    for (int i = 0; i < C::kBLoads; ++i) load_lds16(gb, b_off[i], st + C::kABytes + 1024 * (i * C::kWaves + wv));
+    if (sa_loader) {
+      load_lds4(saw + (int64_t)kb * g.sa_ld + m0, scale_off, st + C::kSaOff + 256 * wv);
+    } else if (sb_loader) {
+      load_lds4(sbw + (int64_t)kb * g.sb_ld + n0, scale_off, st + C::kSbOff + 256 * (wv - C::kSaLoads));
+    }
+  };
+
+  v4f acc[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+  const int gsh = 8 * (lane >> 4);   // this lane's 32-K group within the block
+  issue(0, smem);
+  for (int kb = 0; kb < KB; ++kb) {
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    const uint8_t *st = smem + (kb & 1) * C::kStageBytes;
+    if (kb + 1 < KB) issue(kb + 1, smem + ((kb + 1) & 1) * C::kStageBytes);
+    int ea[4], eb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ea[i] = (int)((*reinterpret_cast<const uint32_t *>(st + C::kSaOff + 4 * (wm + 16 * i + (lane & 15))) >> gsh) & 0xFFu);
+      eb[i] = (int)((*reinterpret_cast<const uint32_t *>(st + C::kSbOff + 4 * (wn + 16 * i + (lane & 15))) >> gsh) & 0xFFu);
+    }
+    v8i af[4], bf[4];
+    af[0] = frag_g32(st, wm + (lane & 15), lane);
+    bf[0] = frag_g32(st + C::kABytes, wn + (lane & 15), lane);
+    bf[1] = frag_g32(st + C::kABytes, wn + 16 + (lane & 15), lane);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      if (q < 2) bf[q + 2] = frag_g32(st + C::kABytes, wn + 16 * (q + 2) + (lane & 15), lane);
+      else if (q < 5) af[q - 1] = frag_g32(st, wm + 16 * (q - 1) + (lane & 15), lane);
+      const int mi = q >> 2, ni = (mi & 1) ? 3 - (q & 3) : (q & 3), i = 4 * mi + ni;
+      // first operand B (its lane's column scale), second A (its lane's row scale)
+      acc[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[ni], af[mi], acc[i], 0, 0, 0, eb[ni], 0, ea[mi]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi) {
+    const int64_t i = m0 + wm + 16 * mi + (lane & 15);
+    if (i >= m) continue;
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) {
+      const int64_t j = n0 + wn + 16 * ni + 4 * (lane >> 4);
+      if (j >= n) continue;
+      const v4f a = acc[4 * mi + ni];
+      uint16_t *dp = reinterpret_cast<uint16_t *>(g.D) + i * g.ldd + j;
+      if (j + 4 <= n) {
+        *reinterpret_cast<u32x2 *>(dp) = (u32x2){bf16_rne(a[0]) | (bf16_rne(a[1]) << 16),
+                                                 bf16_rne(a[2]) | (bf16_rne(a[3]) << 16)};
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (j + r < n) dp[r] = (uint16_t)bf16_rne(a[r]);
+      }
+    }
+  }
+}
+
 // Skinny (decode-sized) problems, m <= 16*MT: there is too little output to fill
 // 256 CUs with 128x128 tiles (m = 1, n = 7168 gives 56 tiles), and the time goes
 // into streaming B once from HBM.  A workgroup owns 16*NT columns (inside one
@@ -566,6 +693,15 @@ hipError_t launch_skinny(const GemmArgs &a, hipStream_t st) {
   } else {
     hipLaunchKernelGGL((gemm_skinny_kernel<MT, NT, W, DEPTH, kSfFp32>), grid, dim3(64 * W), 0, st, a, tiles_n);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_g32(const GemmArgs &a, hipStream_t st) {
+  using C = Cfg<2, 2, 2>;
+  const int tiles_m = (int)((a.m + C::kBM - 1) / C::kBM), tiles_n = (int)((a.n + C::kBN - 1) / C::kBN);
+  const int per_xcd = (tiles_m * tiles_n + kXcds - 1) / kXcds;
+  hipLaunchKernelGGL((gemm_g32_kernel<C>), dim3((unsigned)(per_xcd * kXcds)), dim3(C::kThreads), 0, st, a, tiles_m,
+                     tiles_n);
   return hipGetLastError();
 }
 

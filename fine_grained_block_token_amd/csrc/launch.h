@@ -88,5 +88,8 @@ hipError_t launch_cast_per_token(const CastTokenArgs &a, hipStream_t st);
 hipError_t launch_cast_per_block(const CastBlockArgs &a, hipStream_t st);
 hipError_t launch_cast_dual(const CastDualArgs &a, hipStream_t st);
 hipError_t launch_gemm(const GemmArgs &a, hipStream_t st);
+// UE8M0 group-32 recipe: sa and sb are packed words (one per row and 128-K block,
+// MN-major: (i, kb) at sa[kb*sa_ld + i], (j, kb) at sb[kb*sb_ld + j]).
+hipError_t launch_gemm_g32(const GemmArgs &a, hipStream_t st);
 
 }  // namespace fgfp8

@@ -201,6 +201,29 @@ int gemm_fp8_nt_bf16_cast(const uint8_t *A, int64_t lda, const void *sa, int sa_
                           int64_t m, int64_t n, int64_t k, void *stream);
 
 /*
+ * gemm_fp8_nt_bf16_ue8m0_g32 -- D = (A * sa)(B * sb)^T with one power-of-two
+ * scale per row and 32-wide K group on BOTH operands (the UE8M0 group-32
+ * recipe that "deep-gemm: fused per-token FP8 cast in Triton" benchmarks):
+ *     D[i, j] = sum_g 2^(ea(i,g) + eb(j,g)) sum_{t in g} A[i, t] B[j, t],
+ * rounded to bf16 (nearest, ties to even).  Both operands are what
+ * cast_per_token produces with gran_k = 32 and FGFP8_SF_PACKED_UE8M0 scales in
+ * the MN-major layout.  The scales are applied by the gfx950 scaled FP8 MFMA,
+ * which accumulates in fp32 across all of K.
+ *
+ * A    E4M3 [m, k] row-major, k <= lda < 2^24, lda a multiple of 16; 16-B aligned.
+ * sa   int32 words, (i, kb) at sa[kb*sa_ld + i], sa_ld >= m: byte b of word
+ *      (i, kb) is ea(i, 4kb + b) + 127.
+ * B    E4M3 [n, k], as A.
+ * sb   int32 words, (j, kb) at sb[kb*sb_ld + j], sb_ld >= n.
+ * D    bf16 [m, n] row-major, ldd >= n, multiple of 8; 16-B aligned.
+ * k must be a positive multiple of 128.
+ */
+int gemm_fp8_nt_bf16_ue8m0_g32(const uint8_t *A, int64_t lda, const uint32_t *sa, int64_t sa_ld,
+                               const uint8_t *B, int64_t ldb, const uint32_t *sb, int64_t sb_ld,
+                               uint16_t *D, int64_t ldd, int64_t m, int64_t n, int64_t k,
+                               void *stream);
+
+/*
  * m_grouped_gemm_fp8_nt_bf16_contiguous -- the forward GEMM of a mixture of
  * experts over a token-contiguous LHS.  Defined by "DeepGEMM Essentials",
  * Parts 8-11: the tokens routed to expert e are consecutive rows of A, each
