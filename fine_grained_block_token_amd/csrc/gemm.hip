@@ -62,6 +62,7 @@ struct Cfg {
   static_assert(kALoads * 1024 * kWaves == kABytes && kBLoads * 1024 * kWaves == kBBytes, "tile split");
   static constexpr int kStages = STAGES;
   static constexpr int WAVES_N_ = WAVES_N;
+  static constexpr int kMinBlocks = kWaves <= 4 ? 2 : 1;   // workgroups per CU the registers are sized for
 };
 
 // Byte offset of 16-byte chunk `chunk` (0..7) of tile row `row`.  The gfx950 LDS
@@ -205,7 +206,7 @@ __device__ __forceinline__ void fused_cast_epilogue(const GemmArgs &g, const v4f
 }
 
 template <class C, int SA_FMT, bool WGRAD, bool GROUPED, int CASTF>
-__global__ __launch_bounds__(C::kThreads, 2) void gemm_kernel(GemmArgs g, int tiles_m, int tiles_n) {
+__global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_kernel(GemmArgs g, int tiles_m, int tiles_n) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::kStages * C::kStageBytes];
   const int t = threadIdx.x, lane = t & 63;
   const int wv = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -433,7 +434,7 @@ __device__ __forceinline__ v8i frag_g32(const uint8_t *tile, int row, int lane) 
 }
 
 template <class C>
-__global__ __launch_bounds__(C::kThreads, 2) void gemm_g32_kernel(GemmArgs g, int tiles_m, int tiles_n) {
+__global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_g32_kernel(GemmArgs g, int tiles_m, int tiles_n) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::kStages * C::kStageBytes];
   const int t = threadIdx.x, lane = t & 63;
   const int wv = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -668,13 +669,18 @@ hipError_t launch_cfg(const GemmArgs &a, hipStream_t st) {
   const bool packed = a.sa_fmt == kSfPackedUe8m0;
   if (a.wgrad) {
     FGFP8_GEMM(kSfFp32, true, false, 0);
-  } else if (a.m_idx != nullptr) {
-    if (packed) FGFP8_GEMM(kSfPackedUe8m0, false, true, 0); else FGFP8_GEMM(kSfFp32, false, true, 0);
-  } else if (a.q != nullptr) {
-    if (a.cq_fmt == kSfUe8m0) {
-      if (packed) FGFP8_GEMM(kSfPackedUe8m0, false, false, 2); else FGFP8_GEMM(kSfFp32, false, false, 2);
+  } else if (a.m_idx != nullptr || a.q != nullptr) {
+    // the grouped layout and the fused output cast work on 128x128 tiles
+    if constexpr (C::kBM == 128 && C::kBN == 128) {
+      if (a.m_idx != nullptr) {
+        if (packed) FGFP8_GEMM(kSfPackedUe8m0, false, true, 0); else FGFP8_GEMM(kSfFp32, false, true, 0);
+      } else if (a.cq_fmt == kSfUe8m0) {
+        if (packed) FGFP8_GEMM(kSfPackedUe8m0, false, false, 2); else FGFP8_GEMM(kSfFp32, false, false, 2);
+      } else {
+        if (packed) FGFP8_GEMM(kSfPackedUe8m0, false, false, 1); else FGFP8_GEMM(kSfFp32, false, false, 1);
+      }
     } else {
-      if (packed) FGFP8_GEMM(kSfPackedUe8m0, false, false, 1); else FGFP8_GEMM(kSfFp32, false, false, 1);
+      return hipErrorInvalidValue;
     }
   } else {
     if (packed) FGFP8_GEMM(kSfPackedUe8m0, false, false, 0); else FGFP8_GEMM(kSfFp32, false, false, 0);
