@@ -320,96 +320,135 @@ __global__ __launch_bounds__(kThreads) void cast_tok_cols_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Per-block cast: one workgroup per 128x128 block.  Each thread holds 8 rows
-// x 8 columns in registers; the block amax is a DPP + LDS reduction.  The
-// optional transposed output goes through a 128x128 byte tile in LDS.
+// Per-block cast.  Workgroups are persistent: workgroup w casts 128x128 blocks
+// w, w + G, w + 2G, ... (G = grid size), and the loads of its next block are in
+// flight while the current one is reduced and stored.  Thread t owns 8
+// consecutive rows [8(t>>4), 8(t>>4)+8) x 8 columns [8(t&15), 8(t&15)+8) of a
+// block: each load instruction covers 4 rows of 256 contiguous bytes.  The
+// block amax is a DPP + LDS reduction.  Row-major E4M3 bytes leave as 8-byte
+// stores; the optional transposed copy is an 8x8 byte transpose in registers,
+// whose column k (8 consecutive rows) is one 8-byte store into row k of q^T.
 // ---------------------------------------------------------------------------
-constexpr int kTPitch = 132;  // bytes per row of the transpose tile
+template <typename TIn>
+struct BlockRaw {   // a thread's 8 x 8 elements of one block, as loaded
+  Raw16<TIn> r[4];  // rows 2p, 2p+1 of the 8 in r[p] (8 elements each)
+};
+
+template <typename TIn>
+__device__ __forceinline__ void block_load(const TIn *x, int64_t rows, int64_t cols, int64_t x_ld, int64_t rb,
+                                           int64_t c, BlockRaw<TIn> &br) {
+  const int colvalid = (int)max<int64_t>(0, min<int64_t>(8, cols - c));
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int64_t r = rb + 2 * p + h;
+      constexpr int W = Raw16<TIn>::kWords / 2;   // words per 8 elements
+      const int o = W * h;
+      if (r < rows && colvalid == 8) {
+        const TIn *src = x + r * x_ld + c;
+#pragma unroll
+        for (int i = 0; i < W / 4; ++i) {
+          const uint4 v = reinterpret_cast<const uint4 *>(src)[i];
+          br.r[p].w[o + 4 * i] = v.x; br.r[p].w[o + 4 * i + 1] = v.y;
+          br.r[p].w[o + 4 * i + 2] = v.z; br.r[p].w[o + 4 * i + 3] = v.w;
+        }
+      } else {
+        const bool any = r < rows && colvalid > 0;
+        const TIn *src = x + (any ? r * x_ld + c : 0);
+#pragma unroll
+        for (int i = 0; i < W; ++i) br.r[p].w[o + i] = 0u;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          if (any && e < colvalid) {
+            if constexpr (sizeof(TIn) == 2) br.r[p].w[o + (e >> 1)] |= (uint32_t)src[e] << (16 * (e & 1));
+            else br.r[p].w[o + e] = __float_as_uint(src[e]);
+          }
+        }
+      }
+    }
+  }
+}
 
 template <typename TIn, bool UE8M0, bool TRANS>
 __global__ __launch_bounds__(kThreads) void cast_block_kernel(
-    const TIn *__restrict__ x, int64_t rows, int64_t cols, int64_t x_ld, uint8_t *__restrict__ q,
-    int64_t q_ld, float *__restrict__ sf, int64_t sf_ld, uint8_t *__restrict__ qT, int64_t qT_ld,
-    float *__restrict__ sfT, int64_t sfT_ld) {
-  __shared__ uint32_t red[kThreads / kWave];
-  __shared__ __attribute__((aligned(16))) uint8_t tt[TRANS ? 128 * kTPitch : 4];
+    const TIn *__restrict__ x, int64_t rows, int64_t cols, int64_t x_ld, int64_t tiles_c, int64_t tiles,
+    uint8_t *__restrict__ q, int64_t q_ld, float *__restrict__ sf, int64_t sf_ld, uint8_t *__restrict__ qT,
+    int64_t qT_ld, float *__restrict__ sfT, int64_t sfT_ld) {
+  __shared__ uint32_t red[2][kThreads / kWave];
   const int t = threadIdx.x;
-  const int64_t bi = blockIdx.y, bj = blockIdx.x;
-  const int64_t r0 = bi * 128, c0 = bj * 128;
-  const int cc = t & 15, rr = t >> 4;
-  const int64_t c = c0 + 8 * cc;
-  const bool colfull = c + 8 <= cols;
-  const int colvalid = (int)max<int64_t>(0, min<int64_t>(8, cols - c));
+  const int cc = t & 15, rg = t >> 4;
+  BlockRaw<TIn> cur, nxt;
+  int64_t blk = blockIdx.x;
+  if (blk >= tiles) return;   // uniform over the workgroup
+  block_load<TIn>(x, rows, cols, x_ld, (blk / tiles_c) * 128 + 8 * rg, (blk % tiles_c) * 128 + 8 * cc, cur);
+  for (int it = 0; blk < tiles; ++it, blk += gridDim.x) {
+    const int64_t bi = blk / tiles_c, bj = blk % tiles_c;
+    const int64_t r0 = bi * 128, c0 = bj * 128;
+    const int64_t c = c0 + 8 * cc, rb = r0 + 8 * rg;
+    const int colvalid = (int)max<int64_t>(0, min<int64_t>(8, cols - c));
+    const int64_t nblk = blk + gridDim.x;
+    if (nblk < tiles)
+      block_load<TIn>(x, rows, cols, x_ld, (nblk / tiles_c) * 128 + 8 * rg, (nblk % tiles_c) * 128 + 8 * cc, nxt);
 
-  float v[8][8];
-  uint32_t am = 0;
+    uint32_t am = 0;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int64_t r = r0 + rr + 16 * i;
-    if (r < rows && colvalid > 0) {
-      load8<TIn>(x + r * x_ld + c, colfull, colvalid, v[i]);
-    } else {
+    for (int p = 0; p < 4; ++p)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[i][e] = 0.0f;
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) am = max(am, abs_bits(v[i][e]));
-  }
-  am = wave_max_u32(am);
-  if ((t & 63) == 0) red[t >> 6] = am;
-  __syncthreads();
-  am = max(max(red[0], red[1]), max(red[2], red[3]));
-  const GroupScale gs = group_scale<UE8M0>(__uint_as_float(am));
+      for (int e = 0; e < 16; ++e) am = max(am, abs_bits(cur.r[p].get(e)));
+    am = wave_max_u32(am);
+    uint32_t *rd = red[it & 1];   // alternate buffers: no second barrier before the next block
+    if ((t & 63) == 0) rd[t >> 6] = am;
+    __syncthreads();
+    am = max(max(rd[0], rd[1]), max(rd[2], rd[3]));
+    const GroupScale gs = group_scale<UE8M0>(__uint_as_float(am));
 
+    uint32_t w[8][2];   // row i: columns 0-3, 4-7
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int64_t r = r0 + rr + 16 * i;
-    const uint32_t w0 = e4m3x4(v[i][0] * gs.mult, v[i][1] * gs.mult, v[i][2] * gs.mult, v[i][3] * gs.mult);
-    const uint32_t w1 = e4m3x4(v[i][4] * gs.mult, v[i][5] * gs.mult, v[i][6] * gs.mult, v[i][7] * gs.mult);
-    if (r < rows && colvalid > 0) {
-      uint8_t *qp = q + r * q_ld + c;
-      if (colfull) {
-        *reinterpret_cast<uint2 *>(qp) = make_uint2(w0, w1);
-      } else {
+    for (int i = 0; i < 8; ++i) {
+      const Raw16<TIn> &rr = cur.r[i >> 1];
+      const int o = 8 * (i & 1);
+      w[i][0] = e4m3x4(rr.get(o) * gs.mult, rr.get(o + 1) * gs.mult, rr.get(o + 2) * gs.mult, rr.get(o + 3) * gs.mult);
+      w[i][1] = e4m3x4(rr.get(o + 4) * gs.mult, rr.get(o + 5) * gs.mult, rr.get(o + 6) * gs.mult,
+                       rr.get(o + 7) * gs.mult);
+      const int64_t r = rb + i;
+      if (r < rows && colvalid > 0) {
+        uint8_t *qp = q + r * q_ld + c;
+        if (colvalid == 8) {
+          *reinterpret_cast<uint2 *>(qp) = make_uint2(w[i][0], w[i][1]);
+        } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (e < colvalid) qp[e] = (uint8_t)((e < 4 ? w0 >> (8 * e) : w1 >> (8 * (e - 4))) & 0xFFu);
+          for (int e = 0; e < 8; ++e)
+            if (e < colvalid) qp[e] = (uint8_t)((w[i][e >> 2] >> (8 * (e & 3))) & 0xFFu);
+        }
       }
+    }
+    if (t == 0) {
+      sf[bi * sf_ld + bj] = gs.sf;
+      if constexpr (TRANS) sfT[bj * sfT_ld + bi] = gs.sf;
     }
     if constexpr (TRANS) {
-      uint32_t *tp = reinterpret_cast<uint32_t *>(&tt[(rr + 16 * i) * kTPitch + 8 * cc]);
-      tp[0] = w0;
-      tp[1] = w1;
-    }
-  }
-  if (t == 0) {
-    sf[bi * sf_ld + bj] = gs.sf;
-    if constexpr (TRANS) sfT[bj * sfT_ld + bi] = gs.sf;
-  }
-  if constexpr (TRANS) {
-    __syncthreads();
-    // thread: column ct of the block (a row of q^T), rows [64h, 64h+64)
-    const int ct = t >> 1, h = t & 1;
-    const int64_t rowT = c0 + ct;
-    if (rowT < cols) {
-      uint32_t w[16];
+      const int rvalid = (int)max<int64_t>(0, min<int64_t>(8, rows - rb));
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int rb = 64 * h + 4 * j;
-        w[j] = (uint32_t)tt[(rb + 0) * kTPitch + ct] | ((uint32_t)tt[(rb + 1) * kTPitch + ct] << 8) |
-               ((uint32_t)tt[(rb + 2) * kTPitch + ct] << 16) | ((uint32_t)tt[(rb + 3) * kTPitch + ct] << 24);
-      }
-      const int64_t rbase = r0 + 64 * h;
-      uint8_t *op = qT + rowT * qT_ld + rbase;
-      if (rbase + 64 <= rows) {
+      for (int k = 0; k < 8; ++k) {
+        if (k >= colvalid || rvalid == 0) continue;
+        // byte k of every row: rows 0-3 -> lo, rows 4-7 -> hi
+        const int sh = 8 * (k & 3), wi = k >> 2;
+        const uint32_t lo = ((w[0][wi] >> sh) & 0xFFu) | (((w[1][wi] >> sh) & 0xFFu) << 8) |
+                            (((w[2][wi] >> sh) & 0xFFu) << 16) | (((w[3][wi] >> sh) & 0xFFu) << 24);
+        const uint32_t hi = ((w[4][wi] >> sh) & 0xFFu) | (((w[5][wi] >> sh) & 0xFFu) << 8) |
+                            (((w[6][wi] >> sh) & 0xFFu) << 16) | (((w[7][wi] >> sh) & 0xFFu) << 24);
+        uint8_t *op = qT + (c + k) * qT_ld + rb;
+        if (rvalid == 8) {
+          *reinterpret_cast<uint2 *>(op) = make_uint2(lo, hi);
+        } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          reinterpret_cast<uint4 *>(op)[j] = make_uint4(w[4 * j], w[4 * j + 1], w[4 * j + 2], w[4 * j + 3]);
-      } else if (rbase < rows) {
-        const int valid = (int)(rows - rbase);
-        for (int e = 0; e < valid; ++e) op[e] = (uint8_t)((w[e >> 2] >> (8 * (e & 3))) & 0xFFu);
+          for (int e = 0; e < 8; ++e)
+            if (e < rvalid) op[e] = (uint8_t)((((e < 4) ? lo : hi) >> (8 * (e & 3))) & 0xFFu);
+        }
       }
     }
+    cur = nxt;
   }
 }
 
@@ -552,6 +591,28 @@ __global__ __launch_bounds__(kThreads) void cast_dual_kernel(
   }
 }
 
+// Workgroups of `kernel` (256 threads) resident per CU, and the CU count, as
+// the runtime reports them; callers keep the result in a function-local static
+// of their own (one query per kernel, thread-safe initialisation).
+struct Residency {
+  int per_cu, cus;
+};
+template <typename K>
+Residency residency(K kernel) {
+  int dev = 0, n = 0, c = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, kThreads, 0) != hipSuccess || n < 1 || c < 1)
+    return Residency{2, 256};
+  return Residency{n, c};
+}
+
+// Grid of a persistent kernel: all resident workgroups, at most `work`.
+inline unsigned persistent_grid(const Residency &r, int64_t work) {
+  const int64_t g = (int64_t)r.per_cu * r.cus;
+  return (unsigned)(work < g ? work : g);
+}
+
 template <typename TIn, int GRAN, int FMT>
 hipError_t launch_tok_rows(const void *x, int64_t rows, int64_t cols, int64_t xs_row, uint8_t *q,
                            int64_t q_ld, void *sf, int64_t sf_s_row, int64_t sf_s_grp, hipStream_t st) {
@@ -631,13 +692,17 @@ hipError_t launch_cast_dual(const CastDualArgs &a, hipStream_t st) {
 }
 
 hipError_t launch_cast_per_block(const CastBlockArgs &a, hipStream_t st) {
-  const dim3 grid((unsigned)((a.cols + 127) / 128), (unsigned)((a.rows + 127) / 128));
+  // persistent workgroups, each walking blocks with the next one's loads in flight
+  const int64_t tiles_c = (a.cols + 127) / 128, tiles = tiles_c * ((a.rows + 127) / 128);
   const bool ue = a.sf_fmt == kSfUe8m0;
   const bool tr = a.qT != nullptr;
 #define FGFP8_BLK(T, U, TR)                                                                              \
-  hipLaunchKernelGGL((cast_block_kernel<T, U, TR>), grid, dim3(kThreads), 0, st,                        \
-                     reinterpret_cast<const T *>(a.x), a.rows, a.cols, a.x_ld, a.q, a.q_ld, a.sf, a.sf_ld, \
-                     a.qT, a.qT_ld, a.sfT, a.sfT_ld)
+  do {                                                                                                   \
+    static const Residency res = residency(cast_block_kernel<T, U, TR>);                                \
+  hipLaunchKernelGGL((cast_block_kernel<T, U, TR>), dim3(persistent_grid(res, tiles)), dim3(kThreads), 0, st, \
+                     reinterpret_cast<const T *>(a.x), a.rows, a.cols, a.x_ld, tiles_c, tiles, a.q, a.q_ld, \
+                     a.sf, a.sf_ld, a.qT, a.qT_ld, a.sfT, a.sfT_ld);                                   \
+  } while (0)
   if (a.x_dtype == kInBf16) {
     if (ue) { if (tr) FGFP8_BLK(uint16_t, true, true); else FGFP8_BLK(uint16_t, true, false); }
     else    { if (tr) FGFP8_BLK(uint16_t, false, true); else FGFP8_BLK(uint16_t, false, false); }
