@@ -335,7 +335,9 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_kernel(GemmAr
   static_assert(C::kStages == 2, "two stages");
   issue(0, smem);
   for (int kb = 0; kb < KB; ++kb) {
-    asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // wave priority 0 while waiting and issuing copies, 3 once its MFMAs run (below):
+    // the SIMD's other wave, if it is in its MFMA phase, is served first
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier\n\ts_setprio 0" ::: "memory");
     const uint8_t *st = smem + (kb & 1) * C::kStageBytes;
     // The copy into the free stage goes first: inline assembly bounds the
     // scheduling region, and the fragment reads must share one with the MFMAs.
@@ -360,6 +362,7 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_kernel(GemmAr
       // promote tile i of block kb-1 (scales `prev`) beside block kb's MFMA
       promote<WGRAD>(acc[i], p[i], prev, mi, ni);
       p[i] = mfma_k128(bf[ni], af[mi]);
+      if (q == 0) __builtin_amdgcn_s_setprio(3);
       __builtin_amdgcn_sched_barrier(0);
     }
     prev = cur;
@@ -491,7 +494,7 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_g32_kernel(Ge
   const int gsh = 8 * (lane >> 4);   // this lane's 32-K group within the block
   issue(0, smem);
   for (int kb = 0; kb < KB; ++kb) {
-    asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier\n\ts_setprio 0" ::: "memory");
     const uint8_t *st = smem + (kb & 1) * C::kStageBytes;
     if (kb + 1 < KB) issue(kb + 1, smem + ((kb + 1) & 1) * C::kStageBytes);
     int ea[4], eb[4];
@@ -511,6 +514,7 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_g32_kernel(Ge
       const int mi = q >> 2, ni = (mi & 1) ? 3 - (q & 3) : (q & 3), i = 4 * mi + ni;
       // first operand B (its lane's column scale), second A (its lane's row scale)
       acc[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[ni], af[mi], acc[i], 0, 0, 0, eb[ni], 0, ea[mi]);
+      if (q == 0) __builtin_amdgcn_s_setprio(3);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
