@@ -21,8 +21,8 @@
 //  * A and B K-tiles (128 bytes of K per row) are copied global -> LDS by
 //    global_load_lds_dwordx4 (no VGPR staging), two stages deep.  Each lane
 //    fetches the 16-byte chunk that belongs at its fixed LDS slot under a
-//    16-byte XOR swizzle (chunk ^ (row/2)%8), so fragment reads (ds_read_b128)
-//    are free of bank conflicts.
+//    16-byte XOR swizzle of the row's low bits (swz_key), so fragment reads
+//    (ds_read_b128) are free of bank conflicts.
 //  * 256 threads = 4 waves in a 2x2 grid over a 128x128 output tile, each
 //    wave 64x64 = 4x4 MFMA tiles; 2 workgroups per CU.
 //  * B is the MFMA's first operand, so a lane holds four consecutive output
@@ -65,12 +65,14 @@ struct Cfg {
   static constexpr int kMinBlocks = kWaves <= 4 ? 2 : 1;   // workgroups per CU the registers are sized for
 };
 
-// Byte offset of 16-byte chunk `chunk` (0..7) of tile row `row`.  The gfx950 LDS
-// serves 256 bytes per clock, i.e. 16 lanes of a ds_read_b128 at once; the 16
-// lanes of a fragment read touch rows r..r+15 at one logical chunk, so the XOR
-// key (row/2)%8 together with the row parity (which selects the 128-byte half
-// of the 256-byte bank row) spreads them over all 16 bank groups.
-__device__ __forceinline__ int swz_key(int row) { return (row >> 1) & 7; }
+// Byte offset of 16-byte chunk `chunk` (0..7) of tile row `row`: the chunk index
+// is XORed with a key of the row's low three bits.  A fragment read has lane l
+// on row r + (l & 15) at logical chunk 2(l >> 4) (+1), or l >> 4 (+4) for the
+// group-32 layout.  Measured with ds_read_b128 on MI355X: the key
+// (row & 7) ^ ((row >> 1) & 1) serves both layouts at the rate of a contiguous
+// read (~190 B/clk/CU), at any stage offset; the key (row >> 1) & 7 runs the
+// 16x16x128 layout at ~120 B/clk/CU (2-way bank conflicts).
+__device__ __forceinline__ int swz_key(int row) { return (row & 7) ^ ((row >> 1) & 1); }
 __device__ __forceinline__ int swz(int row, int chunk) { return row * kBK + ((chunk ^ swz_key(row)) << 4); }
 
 // MFMA operand: lane l holds row (l & 15) and K bytes [32*(l>>4), 32*(l>>4)+32).
