@@ -190,6 +190,28 @@ def test_gemm_skinny_one_hot(gpu):
 
 
 # ---------------------------------------------------------------------------
+# More tiles than run at once (2 per CU): 250 x 38360 has 2 x 300 = 600 ragged
+# tiles over 3 K blocks, so the XCD tile ranges, bands and both edges are exercised.
+_MANY_MNK = (250, 38360, 384)
+
+
+def test_gemm_many_ragged_tiles(gpu):
+    qa, sa, qb, sb = _cast_operands(*_MANY_MNK)
+    got = _run_gemm(qa, sa, qb, sb)
+    ref, absum = oracle.gemm_nt(qa, sa, qb, sb)
+    check_bf16_gemm(got, ref, absum, mfma_truncation_bound(qa, sa, qb, sb), _MANY_MNK[2] // 128,
+                    f"gemm many ragged tiles {_MANY_MNK}")
+
+
+def test_gemm_many_ragged_tiles_packed_ue8m0(gpu):
+    qa, words, qb, sb = _cast_operands(*_MANY_MNK, a_fmt=oracle.SF_PACKED_UE8M0)
+    sa = oracle.unpack_ue8m0(words, _MANY_MNK[2] // 128)
+    got = _run_gemm(qa, words, qb, sb, sa_fmt=fg.SF_PACKED_UE8M0)
+    ref, absum = oracle.gemm_nt(qa, sa, qb, sb)
+    check_bf16_gemm(got, ref, absum, mfma_truncation_bound(qa, sa, qb, sb), _MANY_MNK[2] // 128,
+                    f"gemm many ragged tiles packed {_MANY_MNK}")
+
+
 # wgrad
 # ---------------------------------------------------------------------------
 
@@ -237,6 +259,17 @@ def test_wgrad_full_compare(gpu, shape):
     ref, absum = oracle.wgrad_nt(qa, sa, qb, sb, d_in_np)
     tb = mfma_truncation_bound(qa, sa, qb, sb, sb_block=False)
     _check_wgrad(got, ref, absum, tb, -(-tokens // 128), f"wgrad {shape}")
+
+
+def test_wgrad_many_ragged_tiles(gpu):
+    # d_out x d_in = 250 x 38360: 600 ragged tiles, 3 K blocks
+    tokens, d_out, d_in = 384, 250, 38360
+    qa, sa, qb, sb = _wgrad_operands(tokens, d_out, d_in)
+    d_in_np = si.randn((d_out, d_in), 6, 0.1, torch.float32).numpy()
+    got = _run_wgrad(qa, sa, qb, sb, d_in_np)
+    ref, absum = oracle.wgrad_nt(qa, sa, qb, sb, d_in_np)
+    tb = mfma_truncation_bound(qa, sa, qb, sb, sb_block=False)
+    _check_wgrad(got, ref, absum, tb, tokens // 128, "wgrad many ragged tiles (384, 250, 38360)")
 
 
 def test_wgrad_linear_size_sampled(gpu):
