@@ -266,6 +266,22 @@ def extra_kernels(fg, torch, si):
         out[f"gemm_ue8m0_g32_{m}x{n}x{k}"] = _measure(torch, "TFLOPS", 2.0 * m * n * k,
                                                       lambda: fg.gemm_fp8_nt_bf16_ue8m0_g32(A, wa, B, wb, D))
         del a, b, A, B, wa, wb, D
+    # its weight gradient at the linear step's shape: dW [4096, 7168] += dY^T x over 8192 tokens,
+    # operands cast along tokens from the transposed views
+    T, I, O = si.LINEAR["tokens"], si.LINEAR["d_in"], si.LINEAR["d_out"]
+    dy = si.randn((T, O), si.SEED_DY).cuda()
+    x = si.randn((T, I), si.SEED_A).cuda()
+    A = torch.empty((O, T), dtype=torch.uint8, device="cuda")
+    B = torch.empty((I, T), dtype=torch.uint8, device="cuda")
+    wa = fg.mn_major_scales(O, T // 128, torch.int32)
+    wb = fg.mn_major_scales(I, T // 128, torch.int32)
+    fg.cast_per_token(dy.t(), A, wa, 32, fg.SF_PACKED_UE8M0)
+    fg.cast_per_token(x.t(), B, wb, 32, fg.SF_PACKED_UE8M0)
+    D = torch.zeros((O, I), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    out[f"wgrad_ue8m0_g32_{O}x{I}x{T}"] = _measure(torch, "TFLOPS", 2.0 * O * I * T,
+                                                   lambda: fg.wgrad_gemm_fp8_nt_fp32_ue8m0_g32(A, wa, B, wb, D))
+    del dy, x, A, B, wa, wb, D
     # m-grouped contiguous GEMM: the 8-expert token mix of the grouped-GEMM exercise
     # (hidden 2048), as given and with 32x the tokens per expert
     for scale in (1, 32):

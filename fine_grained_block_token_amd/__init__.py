@@ -47,11 +47,12 @@ def load():
     lib.gemm_fp8_nt_bf16_cast.argtypes = [p, i64, p, i32, i64, p, i64, p, i64, p, i64, i32, p, i64, p, i64, i64,
                                           i64, i64, i64, p]
     lib.gemm_fp8_nt_bf16_ue8m0_g32.argtypes = [p, i64, p, i64, p, i64, p, i64, p, i64, i64, i64, i64, p]
+    lib.wgrad_gemm_fp8_nt_fp32_ue8m0_g32.argtypes = [p, i64, p, i64, p, i64, p, i64, p, i64, i64, i64, i64, p]
     lib.m_grouped_gemm_fp8_nt_bf16_contiguous.argtypes = [p, i64, p, i32, i64, p, i64, i64, p, i64, i64, p, i64,
                                                           p, i64, i64, i64, i64, p]
     for f in ("cast_per_token", "cast_per_block", "cast_per_token_dual", "gemm_fp8_nt_bf16",
               "wgrad_gemm_fp8_nt_fp32", "m_grouped_gemm_fp8_nt_bf16_contiguous", "gemm_fp8_nt_bf16_cast",
-              "gemm_fp8_nt_bf16_ue8m0_g32"):
+              "gemm_fp8_nt_bf16_ue8m0_g32", "wgrad_gemm_fp8_nt_fp32_ue8m0_g32"):
         getattr(lib, f).restype = i32
     lib.fgfp8_status_string.argtypes = [i32]
     lib.fgfp8_status_string.restype = ctypes.c_char_p
@@ -61,7 +62,7 @@ def load():
 
 EXPORTED = ("cast_per_token", "cast_per_block", "cast_per_token_dual", "gemm_fp8_nt_bf16",
             "wgrad_gemm_fp8_nt_fp32", "m_grouped_gemm_fp8_nt_bf16_contiguous", "gemm_fp8_nt_bf16_cast",
-            "gemm_fp8_nt_bf16_ue8m0_g32", "fgfp8_status_string")
+            "gemm_fp8_nt_bf16_ue8m0_g32", "wgrad_gemm_fp8_nt_fp32_ue8m0_g32", "fgfp8_status_string")
 
 
 def _check(rc: int, what: str):
@@ -198,6 +199,23 @@ def gemm_fp8_nt_bf16_ue8m0_g32(A: torch.Tensor, sa: torch.Tensor, B: torch.Tenso
     _check(load().gemm_fp8_nt_bf16_ue8m0_g32(_ptr(A), A.stride(0), _ptr(sa), sa_ld, _ptr(B), B.stride(0), _ptr(sb),
                                              sb_ld, _ptr(D), D.stride(0), m, n, k, _stream(A)),
            "gemm_fp8_nt_bf16_ue8m0_g32")
+
+
+def wgrad_gemm_fp8_nt_fp32_ue8m0_g32(A: torch.Tensor, sa: torch.Tensor, B: torch.Tensor, sb: torch.Tensor,
+                                     D: torch.Tensor) -> None:
+    """D[m, n] (fp32) += (A*sa)(B*sb)^T, K over tokens, with the UE8M0 group-32 scales of
+    gemm_fp8_nt_bf16_ue8m0_g32 on both operands (packed words in MN-major views)."""
+    A, B = _u8(A), _u8(B)
+    m, k = A.shape
+    n = B.shape[0]
+    for s_ in (sa, sb):
+        if s_.shape[0] > 1 and s_.stride(0) != 1:
+            raise ValueError("scales must be MN-major (stride(0) == 1)")
+    sa_ld = sa.stride(1) if sa.dim() == 2 else m
+    sb_ld = sb.stride(1) if sb.dim() == 2 else n
+    _check(load().wgrad_gemm_fp8_nt_fp32_ue8m0_g32(_ptr(A), A.stride(0), _ptr(sa), sa_ld, _ptr(B), B.stride(0),
+                                                   _ptr(sb), sb_ld, _ptr(D), D.stride(0), m, n, k, _stream(A)),
+           "wgrad_gemm_fp8_nt_fp32_ue8m0_g32")
 
 
 def m_grouped_gemm_fp8_nt_bf16_contiguous(A: torch.Tensor, sa: torch.Tensor, B: torch.Tensor, sb: torch.Tensor,

@@ -427,7 +427,9 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_kernel(GemmAr
 // scaling then happens inside the MFMA, which accumulates straight into the
 // fp32 accumulator: no promotion.  Each register half holds 16 consecutive
 // K bytes, so the MFMA's runs of 8 products are still 8 consecutive K.  Tiles,
-// copies, waits and fragment order are those of gemm_kernel.
+// copies, waits and fragment order are those of gemm_kernel.  The weight-gradient
+// form ("DeepGEMM Essentials", Parts 12-13: K runs over tokens, fp32 output
+// accumulated in place) differs only in its epilogue.
 __device__ __forceinline__ v8i frag_g32(const uint8_t *tile, int row, int lane) {
   const int c = lane >> 4;
   const u32x4 lo = *reinterpret_cast<const u32x4 *>(tile + swz(row, c));
@@ -438,7 +440,7 @@ __device__ __forceinline__ v8i frag_g32(const uint8_t *tile, int row, int lane) 
   return r;
 }
 
-template <class C>
+template <class C, bool WGRAD>
 __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_g32_kernel(GemmArgs g, int tiles_m, int tiles_n) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::kStages * C::kStageBytes];
   const int t = threadIdx.x, lane = t & 63;
@@ -530,14 +532,26 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_g32_kernel(Ge
       const int64_t j = n0 + wn + 16 * ni + 4 * (lane >> 4);
       if (j >= n) continue;
       const v4f a = acc[4 * mi + ni];
-      uint16_t *dp = reinterpret_cast<uint16_t *>(g.D) + i * g.ldd + j;
-      if (j + 4 <= n) {
-        *reinterpret_cast<u32x2 *>(dp) = (u32x2){bf16_rne(a[0]) | (bf16_rne(a[1]) << 16),
-                                                 bf16_rne(a[2]) | (bf16_rne(a[3]) << 16)};
-      } else {
+      if constexpr (!WGRAD) {
+        uint16_t *dp = reinterpret_cast<uint16_t *>(g.D) + i * g.ldd + j;
+        if (j + 4 <= n) {
+          *reinterpret_cast<u32x2 *>(dp) = (u32x2){bf16_rne(a[0]) | (bf16_rne(a[1]) << 16),
+                                                   bf16_rne(a[2]) | (bf16_rne(a[3]) << 16)};
+        } else {
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (j + r < n) dp[r] = (uint16_t)bf16_rne(a[r]);
+          for (int r = 0; r < 4; ++r)
+            if (j + r < n) dp[r] = (uint16_t)bf16_rne(a[r]);
+        }
+      } else {   // weight gradient: fp32, added to what D holds
+        float *dp = reinterpret_cast<float *>(g.D) + i * g.ldd + j;
+        if (j + 4 <= n) {
+          const v4f d = *reinterpret_cast<const v4f *>(dp);
+          *reinterpret_cast<v4f *>(dp) = d + a;
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (j + r < n) dp[r] += a[r];
+        }
       }
     }
   }
@@ -712,8 +726,12 @@ hipError_t launch_gemm_g32(const GemmArgs &a, hipStream_t st) {
   using C = Cfg<2, 2, 2>;
   const int tiles_m = (int)((a.m + C::kBM - 1) / C::kBM), tiles_n = (int)((a.n + C::kBN - 1) / C::kBN);
   const int per_xcd = (tiles_m * tiles_n + kXcds - 1) / kXcds;
-  hipLaunchKernelGGL((gemm_g32_kernel<C>), dim3((unsigned)(per_xcd * kXcds)), dim3(C::kThreads), 0, st, a, tiles_m,
-                     tiles_n);
+  if (a.wgrad)
+    hipLaunchKernelGGL((gemm_g32_kernel<C, true>), dim3((unsigned)(per_xcd * kXcds)), dim3(C::kThreads), 0, st, a,
+                       tiles_m, tiles_n);
+  else
+    hipLaunchKernelGGL((gemm_g32_kernel<C, false>), dim3((unsigned)(per_xcd * kXcds)), dim3(C::kThreads), 0, st, a,
+                       tiles_m, tiles_n);
   return hipGetLastError();
 }
 

@@ -224,6 +224,25 @@ int gemm_fp8_nt_bf16_ue8m0_g32(const uint8_t *A, int64_t lda, const uint32_t *sa
                                void *stream);
 
 /*
+ * wgrad_gemm_fp8_nt_fp32_ue8m0_g32 -- the weight-gradient form of the UE8M0
+ * group-32 recipe: D += (A * sa)(B * sb)^T in fp32, with K running over tokens
+ * ("DeepGEMM Essentials", Parts 12-13: dW = dY^T x, fp32 output accumulated in
+ * place), and one power-of-two scale per row and 32-wide K group on both
+ * operands, applied by the scaled FP8 MFMA:
+ *     D[i, j] += sum_g 2^(ea(i,g) + eb(j,g)) sum_{t in g} A[i, t] B[j, t].
+ * Both operands are what cast_per_token produces from the transposed views
+ * (dY^T, x^T) with gran_k = 32 and FGFP8_SF_PACKED_UE8M0 scales, MN-major.
+ *
+ * A, sa, sa_ld, B, sb, sb_ld, m, n, k   as gemm_fp8_nt_bf16_ue8m0_g32.
+ * D    fp32 [m, n] row-major, read and written; ldd >= n, multiple of 4;
+ *      16-B aligned.
+ */
+int wgrad_gemm_fp8_nt_fp32_ue8m0_g32(const uint8_t *A, int64_t lda, const uint32_t *sa, int64_t sa_ld,
+                                     const uint8_t *B, int64_t ldb, const uint32_t *sb, int64_t sb_ld,
+                                     float *D, int64_t ldd, int64_t m, int64_t n, int64_t k,
+                                     void *stream);
+
+/*
  * m_grouped_gemm_fp8_nt_bf16_contiguous -- the forward GEMM of a mixture of
  * experts over a token-contiguous LHS.  Defined by "DeepGEMM Essentials",
  * Parts 8-11: the tokens routed to expert e are consecutive rows of A, each

@@ -293,3 +293,14 @@ def gemm_nt_g32(A, sa, B, sb, idx=None):
     ii = np.asarray(idx[0], dtype=np.int64)
     jj = np.asarray(idx[1], dtype=np.int64)
     return np.einsum("ij,ij->i", a[ii], b[jj]), np.einsum("ij,ij->i", np.abs(a[ii]), np.abs(b[jj]))
+
+
+def wgrad_nt_g32(A, sa, B, sb, d_in, idx=None):
+    """Weight-gradient form of gemm_nt_g32 ("DeepGEMM Essentials", Parts 12-13: K
+    runs over tokens and the fp32 output is accumulated): D_in + gemm_nt_g32.
+    Returns (ref, absum) with |D_in| included in absum."""
+    ref, absum = gemm_nt_g32(A, sa, B, sb, idx=idx)
+    d = np.asarray(d_in, dtype=np.float64)
+    if idx is not None:
+        d = d[idx[0], idx[1]]
+    return d + ref, absum + np.abs(d)

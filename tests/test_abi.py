@@ -27,7 +27,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for f in ("cast_per_token", "cast_per_block", "cast_per_token_dual", "gemm_fp8_nt_bf16",
               "wgrad_gemm_fp8_nt_fp32", "m_grouped_gemm_fp8_nt_bf16_contiguous", "gemm_fp8_nt_bf16_cast",
-              "gemm_fp8_nt_bf16_ue8m0_g32", "fgfp8_status_string"):
+              "gemm_fp8_nt_bf16_ue8m0_g32", "wgrad_gemm_fp8_nt_fp32_ue8m0_g32", "fgfp8_status_string"):
         assert f in names
 
 
@@ -202,3 +202,21 @@ def test_g32_rejects(lib, kw):
 
 def test_g32_zero_size_is_ok(lib):
     assert g32(lib, m=0) == 0 and g32(lib, n=0) == 0
+
+
+def wg32(lib, **kw):
+    a = dict(A=P, lda=256, sa=S, sald=128, B=Q, ldb=256, sb=S, sbld=256, D=P, ldd=256, m=128, n=256, k=256, st=None)
+    a.update(kw)
+    return lib.wgrad_gemm_fp8_nt_fp32_ue8m0_g32(a["A"], a["lda"], a["sa"], a["sald"], a["B"], a["ldb"], a["sb"],
+                                                a["sbld"], a["D"], a["ldd"], a["m"], a["n"], a["k"], a["st"])
+
+
+@pytest.mark.parametrize("kw", [dict(sbld=255), dict(sald=127), dict(k=96), dict(sa=None), dict(sb=None), dict(D=None),
+                                dict(ldd=254), dict(ldd=255), dict(D=ctypes.c_void_p(0x10008)),
+                                dict(A=ctypes.c_void_p(0x10008)), dict(lda=1 << 24)])
+def test_wgrad_g32_rejects(lib, kw):
+    assert wg32(lib, **kw) == -1
+
+
+def test_wgrad_g32_zero_size_is_ok(lib):
+    assert wg32(lib, m=0) == 0 and wg32(lib, n=0) == 0

@@ -82,3 +82,82 @@ def test_g32_prefill_sampled(gpu):
     ref, absum = oracle.gemm_nt_g32(qa, sa, qb, sb, idx=(ii, jj))
     tb = mfma_truncation_bound(qa, sa, qb, sb, sb_block=False, idx=(ii, jj), group=32)
     check_bf16_gemm(got[ii, jj], ref, absum, tb, k // 8, f"g32 prefill {(m, n, k)}")
+
+
+# weight gradient in the group-32 recipe: D += (A*sa)(B*sb)^T in fp32, K over tokens.
+# Tolerance per element: (K/8 + 20) 2^-24 (sum|terms| + |D_in|) + the MFMA's
+# run-truncation bound with the group-32 scales (same derivation as the fp32-scale
+# wgrad, with one fp32 rounding per run of 8 tokens).
+
+def _wgrad_operands(tokens, d_out, d_in):
+    dy = si.host_array(si.randn((tokens, d_out), si.SEED_DY))
+    x = si.host_array(si.randn((tokens, d_in), si.SEED_A))
+    qa, wa = oracle.cast_per_token(dy, 32, oracle.SF_PACKED_UE8M0, transpose=True)   # [d_out, tokens]
+    qb, wb = oracle.cast_per_token(x, 32, oracle.SF_PACKED_UE8M0, transpose=True)    # [d_in, tokens]
+    return qa, wa, qb, wb
+
+
+def _run_wgrad(qa, wa, qb, wb, d_in_np, times=1):
+    m, k = qa.shape
+    n = qb.shape[0]
+    ldd = -(-n // 4) * 4 + 4
+    D = torch.full((m, ldd), -1.0, dtype=torch.float32)
+    D[:, :n] = torch.from_numpy(d_in_np)
+    Dd = D.cuda()
+    A, B, sa, sb = torch.from_numpy(qa).cuda(), torch.from_numpy(qb).cuda(), _dev_words(wa), _dev_words(wb)
+    for _ in range(times):
+        say("wgrad_gemm_fp8_nt_fp32_ue8m0_g32", (m, n, k))
+        fg.wgrad_gemm_fp8_nt_fp32_ue8m0_g32(A, sa, B, sb, Dd[:, :n])
+    torch.cuda.synchronize()
+    out = Dd.cpu().numpy()
+    assert (out[:, n:] == -1.0).all()
+    return out[:, :n]
+
+
+def _check_wgrad(got, ref, absum, trunc, k, what):
+    err = np.abs(got.astype(np.float64) - ref)
+    bad = err > (k // 8 + 20) * 2.0 ** -24 * absum + trunc
+    assert not bad.any(), f"{what}: {bad.sum()} elements out of tolerance"
+    rel = np.linalg.norm(got.astype(np.float64) - ref) / np.linalg.norm(ref)
+    print(f"[wgrad-g32-parity] {what}: relative Frobenius {rel:.3e}", flush=True)
+
+
+@pytest.mark.parametrize("shape", [(256, 512, 1024), (384, 130, 200), (1024, 256, 128), (384, 250, 38360)])
+def test_wgrad_g32_full_compare(gpu, shape):
+    tokens, d_out, d_in = shape
+    qa, wa, qb, wb = _wgrad_operands(tokens, d_out, d_in)
+    sa, sb = oracle.unpack_ue8m0(wa, tokens // 32), oracle.unpack_ue8m0(wb, tokens // 32)
+    d_in_np = si.randn((d_out, d_in), 7, 0.1, torch.float32).numpy()
+    got = _run_wgrad(qa, wa, qb, wb, d_in_np)
+    ref, absum = oracle.wgrad_nt_g32(qa, sa, qb, sb, d_in_np)
+    tb = mfma_truncation_bound(qa, sa, qb, sb, sb_block=False, group=32)
+    _check_wgrad(got, ref, absum, tb, tokens, f"wgrad g32 {shape}")
+
+
+def test_wgrad_g32_closed_form_accumulates(gpu):
+    # all-ones operands with a power of two per (row, 32-group) and (column, 32-group):
+    # every partial sum is exact, so two calls give D_in + 2 * closed form exactly
+    m, n, k = 130, 260, 512
+    rng = np.random.default_rng(23)
+    ea = rng.integers(-4, 5, (m, k // 32))
+    eb = rng.integers(-4, 5, (n, k // 32))
+    pack = lambda e: (e + 127).astype(np.uint32).reshape(e.shape[0], -1, 4) @ (1 << (8 * np.arange(4, dtype=np.uint32)))
+    wa, wb = pack(ea).astype(np.uint32), pack(eb).astype(np.uint32)
+    d_in = rng.integers(-64, 65, (m, n)).astype(np.float32)
+    got = _run_wgrad(np.full((m, k), 0x38, np.uint8), wa, np.full((n, k), 0x38, np.uint8), wb, d_in, times=2)
+    want = d_in.astype(np.float64) + 2 * 32 * (np.ldexp(1.0, ea)[:, None, :] * np.ldexp(1.0, eb)[None, :, :]).sum(axis=2)
+    assert np.array_equal(got.astype(np.float64), want)
+
+
+def test_wgrad_g32_linear_size_sampled(gpu):
+    tokens, d_out, d_in = si.LINEAR["tokens"], si.LINEAR["d_out"], si.LINEAR["d_in"]
+    qa, wa, qb, wb = _wgrad_operands(tokens, d_out, d_in)
+    sa, sb = oracle.unpack_ue8m0(wa, tokens // 32), oracle.unpack_ue8m0(wb, tokens // 32)
+    zero = np.zeros((d_out, d_in), np.float32)
+    got = _run_wgrad(qa, wa, qb, wb, zero)
+    rng = np.random.default_rng(9)
+    ii = np.concatenate([rng.integers(0, d_out, 20000), [0, d_out - 1, 127, 128]])
+    jj = np.concatenate([rng.integers(0, d_in, 20000), [0, d_in - 1, 128, 127]])
+    ref, absum = oracle.wgrad_nt_g32(qa, sa, qb, sb, zero, idx=(ii, jj))
+    tb = mfma_truncation_bound(qa, sa, qb, sb, sb_block=False, idx=(ii, jj), group=32)
+    _check_wgrad(got[ii, jj], ref, absum, tb, tokens, "wgrad g32 4096x7168x8192")

@@ -59,3 +59,29 @@ def test_sampled_equals_full():
     ii, jj = np.array([0, 32, 5, 17]), np.array([64, 0, 33, 1])
     r, a = oracle.gemm_nt_g32(qa, sa, qb, sb, idx=(ii, jj))
     assert np.allclose(r, ref[ii, jj], rtol=1e-15, atol=1e-300) and np.allclose(a, absum[ii, jj], rtol=1e-15)
+
+
+def test_wgrad_g32_loop_brute_force():
+    # D_in + the per-element sum over tokens, element by element
+    qa, sa, qb, sb = _g32_operands(3, 4, 256, seed=30)
+    d_in = np.array([[0.5 * (i - j) for j in range(4)] for i in range(3)], np.float32)
+    ref, absum = oracle.wgrad_nt_g32(qa, sa, qb, sb, d_in)
+    a, b = _dec(qa), _dec(qb)
+    for i in range(3):
+        for j in range(4):
+            want = float(d_in[i, j]) + sum(float(sa[i, t // 32]) * float(sb[j, t // 32]) * a[i, t] * b[j, t]
+                                           for t in range(256))
+            assert abs(ref[i, j] - want) <= 1e-15 * absum[i, j]
+
+
+def test_wgrad_g32_all_ones_closed_form_with_d_in():
+    m, n, k = 5, 3, 384
+    rng = np.random.default_rng(31)
+    ea = rng.integers(-2, 3, (m, k // 32))
+    eb = rng.integers(-2, 3, (n, k // 32))
+    d_in = rng.integers(-8, 9, (m, n)).astype(np.float32)
+    ref, _ = oracle.wgrad_nt_g32(np.full((m, k), 0x38, np.uint8), np.ldexp(1.0, ea).astype(np.float32),
+                                 np.full((n, k), 0x38, np.uint8), np.ldexp(1.0, eb).astype(np.float32), d_in)
+    want = d_in.astype(np.float64) + np.array(
+        [[sum(32 * 2.0 ** (ea[i, g] + eb[j, g]) for g in range(k // 32)) for j in range(n)] for i in range(m)])
+    assert np.array_equal(ref, want)
