@@ -91,11 +91,34 @@ class Linear:
             ("cast_dYT", lambda: fg.cast_per_token(self.dY.t(), self.dYTq, self.sdYT, 128, fg.SF_FP32)),
         ]
 
+    def g32_ops(self):
+        """The same step in the UE8M0 group-32 recipe: every operand cast per row with 32-wide
+        K groups and packed UE8M0 scales (x, xT, W, WT, dY, dYT: six single-orientation
+        casts), and the three GEMMs on the scaled MFMA.  Reuses the FP8 buffers."""
+        fg, torch = self.fg, self.torch
+        T, I, O = self.T, self.I, self.O
+        w = lambda r, c: fg.mn_major_scales(r, c // 128, torch.int32)
+        self.wx, self.wxT, self.wW, self.wWT, self.wdY, self.wdYT = w(T, I), w(I, T), w(O, I), w(I, O), w(T, O), w(O, T)
+        P = fg.SF_PACKED_UE8M0
+        return [
+            ("cast_x_g32", lambda: fg.cast_per_token(self.x, self.xq, self.wx, 32, P)),
+            ("cast_xT_g32", lambda: fg.cast_per_token(self.x.t(), self.xTq, self.wxT, 32, P)),
+            ("cast_W_g32", lambda: fg.cast_per_token(self.W, self.Wq, self.wW, 32, P)),
+            ("cast_WT_g32", lambda: fg.cast_per_token(self.W.t(), self.WqT, self.wWT, 32, P)),
+            ("gemm_fwd_g32", lambda: fg.gemm_fp8_nt_bf16_ue8m0_g32(self.xq, self.wx, self.Wq, self.wW, self.y)),
+            ("cast_dY_g32", lambda: fg.cast_per_token(self.dY, self.dYq, self.wdY, 32, P)),
+            ("cast_dYT_g32", lambda: fg.cast_per_token(self.dY.t(), self.dYTq, self.wdYT, 32, P)),
+            ("gemm_dgrad_g32", lambda: fg.gemm_fp8_nt_bf16_ue8m0_g32(self.dYq, self.wdY, self.WqT, self.wWT, self.dX)),
+            ("gemm_wgrad_g32", lambda: fg.wgrad_gemm_fp8_nt_fp32_ue8m0_g32(self.dYTq, self.wdYT, self.xTq, self.wxT,
+                                                                          self.dW)),
+        ]
+
     def work(self):
         """Algorithmic flops (GEMMs) and HBM bytes (casts: read input once, write q + scales once)."""
         T, I, O = self.T, self.I, self.O
         f = 2.0 * T * I * O
         tok = lambda r, c: r * c * 2 + r * c + r * (c // 128) * 4
+        tok32 = lambda r, c: r * c * 2 + r * c + r * (c // 128) * 4     # one packed word per 128 columns
         dual = lambda r, c: r * c * 2 + 2 * r * c + (r * (c // 128) + c * (r // 128)) * 4
         blk = O * I * 2 + 2 * O * I + 2 * (O // 128) * (I // 128) * 4
         return {
@@ -103,6 +126,10 @@ class Linear:
             "cast_x": ("GB/s", tok(T, I)), "cast_xT": ("GB/s", tok(I, T)),
             "cast_dY": ("GB/s", tok(T, O)), "cast_dYT": ("GB/s", tok(O, T)),
             "gemm_fwd": ("TFLOPS", f), "gemm_dgrad": ("TFLOPS", f), "gemm_wgrad": ("TFLOPS", f),
+            "cast_x_g32": ("GB/s", tok32(T, I)), "cast_xT_g32": ("GB/s", tok32(I, T)),
+            "cast_W_g32": ("GB/s", tok32(O, I)), "cast_WT_g32": ("GB/s", tok32(I, O)),
+            "cast_dY_g32": ("GB/s", tok32(T, O)), "cast_dYT_g32": ("GB/s", tok32(O, T)),
+            "gemm_fwd_g32": ("TFLOPS", f), "gemm_dgrad_g32": ("TFLOPS", f), "gemm_wgrad_g32": ("TFLOPS", f),
         }
 
 
@@ -412,7 +439,7 @@ def main():
     total_ms, per = timed_ops(torch, ops, args.steps, args.warmup)
     ms_step = total_ms / args.steps
     work = lin.work()
-    flops_step = sum(a for (u, a) in work.values() if u == "TFLOPS")
+    flops_step = sum(work[name][1] for name, _ in ops if work[name][0] == "TFLOPS")
     kernels = {name: rate(*work[name], per[name]) for name in per}
     dom = max((n for n in per if n.startswith("gemm")), key=lambda n: per[n])
     dom_tflops = work[dom][1] / (per[dom] * 1e-3) / 1e12
@@ -444,6 +471,12 @@ def main():
         result["extra"]["linear_step_separate_casts"] = {
             name: _measure(torch, *work[name], fn) for name, fn in lin.separate_cast_ops()}
         result["extra"]["forward_with_output_cast"] = fused_output_cast(fg, torch, lin)
+        g32 = lin.g32_ops()
+        g_ms, g_per = timed_ops(torch, g32, 10, 2)
+        g_ms /= 10
+        result["extra"]["linear_step_ue8m0_g32"] = {
+            "ms_per_step": g_ms, "tflops": flops_step / (g_ms * 1e-3) / 1e12,
+            "kernels": {name: rate(*work[name], g_per[name]) for name in g_per}}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(si)
     print(json.dumps(result), flush=True)
