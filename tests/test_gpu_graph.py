@@ -32,6 +32,21 @@ def test_graph_replays_match_eager(gpu):
     y = torch.empty((T, O), dtype=torch.bfloat16, device="cuda")
     y1 = torch.empty((1, O), dtype=torch.bfloat16, device="cuda")
     dW = torch.empty((I, I), dtype=f32, device="cuda")
+    # dual cast, fused output cast, group-32 GEMM and wgrad, m-grouped GEMM
+    dq, dsx = torch.empty((T, I), dtype=u8, device="cuda"), fg.mn_major_scales(T, I // 128)
+    dqT, dsxT = torch.empty((I, T), dtype=u8, device="cuda"), fg.mn_major_scales(I, T // 128)
+    yq, ysf = torch.empty((T, O), dtype=u8, device="cuda"), fg.mn_major_scales(T, O // 128)
+    y2 = torch.empty((T, O), dtype=torch.bfloat16, device="cuda")
+    W32, sW32 = torch.empty((O, I), dtype=u8, device="cuda"), fg.mn_major_scales(O, I // 128, torch.int32)
+    y32 = torch.empty((T, O), dtype=torch.bfloat16, device="cuda")
+    xT32, sxT32 = torch.empty((I, T), dtype=u8, device="cuda"), fg.mn_major_scales(I, T // 128, torch.int32)
+    dW32 = torch.empty((I, I), dtype=f32, device="cuda")
+    m_idx = torch.from_numpy(si.grouped_layout([100, 200])).cuda()   # 384 rows, 2 experts
+    E = 2
+    Wg = torch.stack([W, W.flip(0)])
+    Wgq = torch.empty((E, O, I), dtype=u8, device="cuda")
+    sWg = torch.empty((E, O // 128, I // 128), dtype=f32, device="cuda")
+    yg = torch.empty((m_idx.numel(), O), dtype=torch.bfloat16, device="cuda")
 
     def step():
         fg.cast_per_token(x, xq, sx, 128, fg.SF_FP32)
@@ -42,8 +57,18 @@ def test_graph_replays_match_eager(gpu):
         fg.gemm_fp8_nt_bf16(xq, sx, Wq, sW, y)
         fg.gemm_fp8_nt_bf16(xq1, sx1, Wq, sW, y1)          # decode-sized path
         fg.wgrad_gemm_fp8_nt_fp32(xTq, sxT, xTq, sxT, dW)  # dW += xT xT^T
+        fg.cast_per_token_dual(x, dq, dsx, dqT, dsxT)
+        fg.gemm_fp8_nt_bf16_cast(xq, sx, Wq, sW, y2, yq, ysf)
+        fg.cast_per_token(W, W32, sW32, 32, fg.SF_PACKED_UE8M0)
+        fg.gemm_fp8_nt_bf16_ue8m0_g32(wp, swp, W32, sW32, y32)
+        fg.cast_per_token(x.t(), xT32, sxT32, 32, fg.SF_PACKED_UE8M0)
+        fg.wgrad_gemm_fp8_nt_fp32_ue8m0_g32(xT32, sxT32, xT32, sxT32, dW32)
+        for e in range(E):
+            fg.cast_per_block(Wg[e], Wgq[e], sWg[e], sf_fmt=fg.SF_FP32)
+        fg.m_grouped_gemm_fp8_nt_bf16_contiguous(xq[:m_idx.numel()], sx[:m_idx.numel()], Wgq, sWg, m_idx, yg)
 
-    outs = [xq, sx, xq1, sx1, wp, swp, xTq, sxT, Wq, sW, y, y1]
+    outs = [xq, sx, xq1, sx1, wp, swp, xTq, sxT, Wq, sW, y, y1, dq, dsx, dqT, dsxT, yq, ysf, y2, W32, sW32, y32,
+            xT32, sxT32, dW32, Wgq, sWg, yg]
 
     def snap():
         return [o.cpu().clone() for o in outs], dW.cpu().clone()
