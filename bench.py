@@ -92,22 +92,20 @@ class Linear:
         ]
 
     def g32_ops(self):
-        """The same step in the UE8M0 group-32 recipe: every operand cast per row with 32-wide
-        K groups and packed UE8M0 scales (x, xT, W, WT, dY, dYT: six single-orientation
-        casts), and the three GEMMs on the scaled MFMA.  Reuses the FP8 buffers."""
+        """The same step in the UE8M0 group-32 recipe: x, W and dY each cast once in both
+        orientations with 32-wide groups and packed UE8M0 scales (x, xT; W, WT; dY, dYT), and
+        the three GEMMs on the scaled MFMA.  Reuses the FP8 buffers."""
         fg, torch = self.fg, self.torch
         T, I, O = self.T, self.I, self.O
         w = lambda r, c: fg.mn_major_scales(r, c // 128, torch.int32)
         self.wx, self.wxT, self.wW, self.wWT, self.wdY, self.wdYT = w(T, I), w(I, T), w(O, I), w(I, O), w(T, O), w(O, T)
         P = fg.SF_PACKED_UE8M0
         return [
-            ("cast_x_g32", lambda: fg.cast_per_token(self.x, self.xq, self.wx, 32, P)),
-            ("cast_xT_g32", lambda: fg.cast_per_token(self.x.t(), self.xTq, self.wxT, 32, P)),
-            ("cast_W_g32", lambda: fg.cast_per_token(self.W, self.Wq, self.wW, 32, P)),
-            ("cast_WT_g32", lambda: fg.cast_per_token(self.W.t(), self.WqT, self.wWT, 32, P)),
+            ("cast_x_dual_g32", lambda: fg.cast_per_token_dual(self.x, self.xq, self.wx, self.xTq, self.wxT, P, 32)),
+            ("cast_W_dual_g32", lambda: fg.cast_per_token_dual(self.W, self.Wq, self.wW, self.WqT, self.wWT, P, 32)),
             ("gemm_fwd_g32", lambda: fg.gemm_fp8_nt_bf16_ue8m0_g32(self.xq, self.wx, self.Wq, self.wW, self.y)),
-            ("cast_dY_g32", lambda: fg.cast_per_token(self.dY, self.dYq, self.wdY, 32, P)),
-            ("cast_dYT_g32", lambda: fg.cast_per_token(self.dY.t(), self.dYTq, self.wdYT, 32, P)),
+            ("cast_dY_dual_g32", lambda: fg.cast_per_token_dual(self.dY, self.dYq, self.wdY, self.dYTq, self.wdYT, P,
+                                                                 32)),
             ("gemm_dgrad_g32", lambda: fg.gemm_fp8_nt_bf16_ue8m0_g32(self.dYq, self.wdY, self.WqT, self.wWT, self.dX)),
             ("gemm_wgrad_g32", lambda: fg.wgrad_gemm_fp8_nt_fp32_ue8m0_g32(self.dYTq, self.wdYT, self.xTq, self.wxT,
                                                                           self.dW)),
@@ -118,7 +116,6 @@ class Linear:
         T, I, O = self.T, self.I, self.O
         f = 2.0 * T * I * O
         tok = lambda r, c: r * c * 2 + r * c + r * (c // 128) * 4
-        tok32 = lambda r, c: r * c * 2 + r * c + r * (c // 128) * 4     # one packed word per 128 columns
         dual = lambda r, c: r * c * 2 + 2 * r * c + (r * (c // 128) + c * (r // 128)) * 4
         blk = O * I * 2 + 2 * O * I + 2 * (O // 128) * (I // 128) * 4
         return {
@@ -126,9 +123,8 @@ class Linear:
             "cast_x": ("GB/s", tok(T, I)), "cast_xT": ("GB/s", tok(I, T)),
             "cast_dY": ("GB/s", tok(T, O)), "cast_dYT": ("GB/s", tok(O, T)),
             "gemm_fwd": ("TFLOPS", f), "gemm_dgrad": ("TFLOPS", f), "gemm_wgrad": ("TFLOPS", f),
-            "cast_x_g32": ("GB/s", tok32(T, I)), "cast_xT_g32": ("GB/s", tok32(I, T)),
-            "cast_W_g32": ("GB/s", tok32(O, I)), "cast_WT_g32": ("GB/s", tok32(I, O)),
-            "cast_dY_g32": ("GB/s", tok32(T, O)), "cast_dYT_g32": ("GB/s", tok32(O, T)),
+            "cast_x_dual_g32": ("GB/s", dual(T, I)), "cast_W_dual_g32": ("GB/s", dual(O, I)),
+            "cast_dY_dual_g32": ("GB/s", dual(T, O)),
             "gemm_fwd_g32": ("TFLOPS", f), "gemm_dgrad_g32": ("TFLOPS", f), "gemm_wgrad_g32": ("TFLOPS", f),
         }
 

@@ -41,7 +41,7 @@ def load():
     p, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     lib.cast_per_token.argtypes = [p, i32, i64, i64, i64, i64, i32, i32, p, i64, p, i64, i64, p]
     lib.cast_per_block.argtypes = [p, i32, i64, i64, i64, i32, p, i64, p, i64, p, i64, p, i64, p]
-    lib.cast_per_token_dual.argtypes = [p, i32, i64, i64, i64, i32, p, i64, p, i64, i64, p, i64, p, i64, i64, p]
+    lib.cast_per_token_dual.argtypes = [p, i32, i64, i64, i64, i32, i32, p, i64, p, i64, i64, p, i64, p, i64, i64, p]
     lib.gemm_fp8_nt_bf16.argtypes = [p, i64, p, i32, i64, p, i64, p, i64, p, i64, i64, i64, i64, p]
     lib.wgrad_gemm_fp8_nt_fp32.argtypes = [p, i64, p, i64, p, i64, p, i64, p, i64, i64, i64, i64, p]
     lib.gemm_fp8_nt_bf16_cast.argtypes = [p, i64, p, i32, i64, p, i64, p, i64, p, i64, i32, p, i64, p, i64, i64,
@@ -135,15 +135,16 @@ def cast_per_block(x: torch.Tensor, q: torch.Tensor, sf: torch.Tensor, qT: torch
 
 
 def cast_per_token_dual(x: torch.Tensor, q: torch.Tensor, sf: torch.Tensor, qT: torch.Tensor,
-                        sfT: torch.Tensor, sf_fmt: int = SF_FP32) -> None:
-    """Both 1x128 per-token casts of row-major bf16 ``x`` [rows, cols] from one read:
-    ``q``/``sf`` as cast_per_token(x) and ``qT`` [cols, rows] / ``sfT`` [cols, ceil(rows/128)]
-    as cast_per_token(x.t())."""
+                        sfT: torch.Tensor, sf_fmt: int = SF_FP32, gran_k: int = 128) -> None:
+    """Both 1 x gran_k per-token casts of row-major bf16 ``x`` [rows, cols] from one read:
+    ``q``/``sf`` as cast_per_token(x, gran_k, sf_fmt) and ``qT`` [cols, rows] / ``sfT`` as
+    cast_per_token(x.t(), gran_k, sf_fmt) (float scales, or int32 packed-UE8M0 words)."""
     q, qT = _u8(q), _u8(qT)
     rows, cols = x.shape
     if x.stride(1) != 1:
         raise ValueError("x must be row-major")
-    _check(load().cast_per_token_dual(_ptr(x), _x_dtype(x), rows, cols, x.stride(0), sf_fmt, _ptr(q), q.stride(0),
+    _check(load().cast_per_token_dual(_ptr(x), _x_dtype(x), rows, cols, x.stride(0), gran_k, sf_fmt, _ptr(q),
+                                      q.stride(0),
                                       _ptr(sf), sf.stride(0), sf.stride(1), _ptr(qT), qT.stride(0),
                                       _ptr(sfT), sfT.stride(0), sfT.stride(1), _stream(x)),
            "cast_per_token_dual")

@@ -107,12 +107,13 @@ static bool scale_layout_ok(int64_t rows, int64_t groups, int64_t s_row, int64_t
   return (s_grp == 1 && s_row >= groups) || (s_row == 1 && s_grp >= rows);
 }
 
-int cast_per_token_dual(const void *x, int x_dtype, int64_t rows, int64_t cols, int64_t x_ld, int sf_fmt,
-                        uint8_t *q, int64_t q_ld, void *sf, int64_t sf_stride_row, int64_t sf_stride_group,
-                        uint8_t *qT, int64_t qT_ld, void *sfT, int64_t sfT_stride_row,
+int cast_per_token_dual(const void *x, int x_dtype, int64_t rows, int64_t cols, int64_t x_ld, int gran_k,
+                        int sf_fmt, uint8_t *q, int64_t q_ld, void *sf, int64_t sf_stride_row,
+                        int64_t sf_stride_group, uint8_t *qT, int64_t qT_ld, void *sfT, int64_t sfT_stride_row,
                         int64_t sfT_stride_group, void *stream) {
   if (x_dtype != kInBf16) return FGFP8_EINVAL;
-  if (sf_fmt != kSfFp32 && sf_fmt != kSfUe8m0) return FGFP8_EINVAL;
+  if (gran_k != 32 && gran_k != 128) return FGFP8_EINVAL;
+  if (sf_fmt != kSfFp32 && sf_fmt != kSfUe8m0 && sf_fmt != kSfPackedUe8m0) return FGFP8_EINVAL;
   if (rows < 0 || cols < 0) return FGFP8_EINVAL;
   if (rows == 0 || cols == 0) return FGFP8_OK;
   if (!x || !q || !sf || !qT || !sfT) return FGFP8_EINVAL;
@@ -120,12 +121,16 @@ int cast_per_token_dual(const void *x, int x_dtype, int64_t rows, int64_t cols, 
   if (!aligned(q, 8) || q_ld < cols || q_ld % 8 != 0) return FGFP8_EINVAL;
   if (!aligned(qT, 16) || qT_ld < rows || qT_ld % 16 != 0) return FGFP8_EINVAL;
   if (!aligned(sf, 4) || !aligned(sfT, 4)) return FGFP8_EINVAL;
-  if (!scale_layout_ok(rows, cdiv(cols, 128), sf_stride_row, sf_stride_group)) return FGFP8_EINVAL;
-  if (!scale_layout_ok(cols, cdiv(rows, 128), sfT_stride_row, sfT_stride_group)) return FGFP8_EINVAL;
+  // scale units per row: groups, or packed words of four groups
+  const bool packed = sf_fmt == kSfPackedUe8m0;
+  const int64_t units = packed ? cdiv(cdiv(cols, gran_k), 4) : cdiv(cols, gran_k);
+  const int64_t unitsT = packed ? cdiv(cdiv(rows, gran_k), 4) : cdiv(rows, gran_k);
+  if (!scale_layout_ok(rows, units, sf_stride_row, sf_stride_group)) return FGFP8_EINVAL;
+  if (!scale_layout_ok(cols, unitsT, sfT_stride_row, sfT_stride_group)) return FGFP8_EINVAL;
   if (cdiv(rows, 128) * cdiv(cols, 128) > 0x7FFFFFFF) return FGFP8_EINVAL;
   const int dev = check_device();
   if (dev != FGFP8_OK) return dev;
-  fgfp8::CastDualArgs a{x, rows, cols, x_ld, sf_fmt, q, q_ld, sf, sf_stride_row, sf_stride_group,
+  fgfp8::CastDualArgs a{x, rows, cols, x_ld, gran_k, sf_fmt, q, q_ld, sf, sf_stride_row, sf_stride_group,
                         qT, qT_ld, sfT, sfT_stride_row, sfT_stride_group};
   return launched(fgfp8::launch_cast_dual(a, static_cast<hipStream_t>(stream)));
 }

@@ -454,33 +454,56 @@ __global__ __launch_bounds__(kThreads) void cast_block_kernel(
 
 // ---------------------------------------------------------------------------
 // Dual-orientation per-token cast of a bf16 [rows, cols] matrix: the row-wise
-// cast (1x128 groups along cols) and the cast of its transpose (1x128 groups
-// along rows: the layout of the weight-gradient operands) from one read of x.
-// A 128x128 tile holds whole groups in both directions; one workgroup per tile.
+// cast (1 x GRAN groups along cols) and the cast of its transpose (1 x GRAN
+// groups along rows: the layout of the weight-gradient operands) from one read
+// of x.  A 128x128 tile holds whole groups in both directions; one workgroup
+// per tile.  GRAN is 128 or 32; FMT is fp32, UE8M0 or packed UE8M0 scales.
 // Phase 1: lane (c = lane&15, j = lane>>4) of wave w loads columns [8c, 8c+8)
 // of tile rows 32w + 2(4i+j) + s (i < 4, s < 2) with 16-byte loads (4 rows of
-// 256 bytes per instruction); a 16-lane DPP max gives each row's amax and the
-// row's E4M3 bytes leave as 8-byte stores.  The bf16 pairs of rows (2v, 2v+1)
-// go to an LDS tile stored column-major (64 words per column) at word
-// v ^ 4h(col), h(f) = ((f>>3)^(f&3))&15, which keeps both the phase-1 dword
-// writes and the phase-2 16-byte reads free of bank conflicts.  Phase 2:
-// thread t owns columns t>>2 and 64+(t>>2), rows [32p, 32p+32) with p = t&3; a
-// 4-lane max gives each column group's amax and its E4M3 bytes leave as two
-// 16-byte stores.
+// 256 bytes per instruction); a 16-lane (GRAN 128) or 4-lane (GRAN 32) DPP max
+// gives each group's amax and the row's E4M3 bytes leave as 8-byte stores.  The
+// bf16 pairs of rows (2v, 2v+1) go to an LDS tile stored column-major (64
+// words per column) at word v ^ 4h(col), h(f) = ((f>>3)^(f&3))&15.  Phase 2:
+// thread t owns columns t>>2 and 64+(t>>2), rows [32p, 32p+32) with p = t&3;
+// a 4-lane max (GRAN 128) or the thread's own 32 values (GRAN 32) give the
+// amax, and the column's E4M3 bytes leave as two 16-byte stores.
+// Packed UE8M0 words hold the exponent bytes of groups 4w..4w+3 (unused bytes
+// zero): with GRAN 32 one word covers a tile's 128 columns (rows) and is
+// assembled with a DPP OR; with GRAN 128 a word spans four tiles, so each tile
+// stores its own byte, and the tile of the last group also zeroes the word's
+// unused bytes.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int dual_word(int f, int v) { return f * 64 + (v ^ (4 * (((f >> 3) ^ (f & 3)) & 15))); }
 
-template <bool UE8M0>
+template <int FMT>
+__device__ __forceinline__ void store_scale(void *sf, int64_t idx, const GroupScale &gs) {
+  reinterpret_cast<float *>(sf)[idx] = gs.sf;
+}
+
+// GRAN 128 packed: byte g%4 of word (row, g/4); the last group's tile zeroes the rest.
+__device__ __forceinline__ void store_packed_byte(void *sf, int64_t row_off, int64_t s_grp, int64_t g, int64_t G,
+                                                  uint32_t e8) {
+  uint8_t *w = reinterpret_cast<uint8_t *>(reinterpret_cast<uint32_t *>(sf) + row_off + (g >> 2) * s_grp);
+  w[g & 3] = (uint8_t)e8;
+  if (g == G - 1)
+    for (int b = (int)(g & 3) + 1; b < 4; ++b) w[b] = 0;
+}
+
+template <int GRAN, int FMT>
 __global__ __launch_bounds__(kThreads) void cast_dual_kernel(
     const uint16_t *__restrict__ x, int64_t rows, int64_t cols, int64_t ld, int64_t tiles_c,
-    uint8_t *__restrict__ q, int64_t q_ld, float *__restrict__ sf, int64_t sf_s_row, int64_t sf_s_grp,
-    uint8_t *__restrict__ qT, int64_t qT_ld, float *__restrict__ sfT, int64_t sfT_s_row, int64_t sfT_s_grp) {
+    uint8_t *__restrict__ q, int64_t q_ld, void *__restrict__ sf, int64_t sf_s_row, int64_t sf_s_grp,
+    uint8_t *__restrict__ qT, int64_t qT_ld, void *__restrict__ sfT, int64_t sfT_s_row, int64_t sfT_s_grp) {
+  static_assert(GRAN == 32 || GRAN == 128, "group 32 or 128");
+  constexpr bool UE8M0 = FMT != kSfFp32;
+  constexpr bool PACKED = FMT == kSfPackedUe8m0;
   __shared__ __attribute__((aligned(16))) uint32_t tile[128 * 64];
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const int64_t r0 = (int64_t)(blockIdx.x / tiles_c) * 128, c0 = (int64_t)(blockIdx.x % tiles_c) * 128;
   const int c = lane & 15, j = lane >> 4;
   const int64_t fc = c0 + 8 * c;
   const int validf = (int)max<int64_t>(0, min<int64_t>(8, cols - fc));
+  const int64_t G = (cols + GRAN - 1) / GRAN, GT = (rows + GRAN - 1) / GRAN;   // groups per row / column
 
   uint32_t raw[4][2][4];
 #pragma unroll
@@ -504,7 +527,7 @@ __global__ __launch_bounds__(kThreads) void cast_dual_kernel(
       for (int k = 0; k < 4; ++k) raw[i][s][k] = w[k];
     }
 
-  // rows: one 128-column group per tile row
+  // rows: 1 x GRAN groups along the tile row (16 lanes x 8 columns, or 4 lanes per group)
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -515,11 +538,18 @@ __global__ __launch_bounds__(kThreads) void cast_dual_kernel(
       uint32_t am = 0;
 #pragma unroll
       for (int e = 0; e < 8; ++e) am = max(am, abs_bits(v[e]));
-      am = group_max_u32<16>(am);
+      am = group_max_u32<GRAN / 8>(am);
       const GroupScale gs = group_scale<UE8M0>(__uint_as_float(am));
       const uint32_t w0 = e4m3x4(v[0] * gs.mult, v[1] * gs.mult, v[2] * gs.mult, v[3] * gs.mult);
       const uint32_t w1 = e4m3x4(v[4] * gs.mult, v[5] * gs.mult, v[6] * gs.mult, v[7] * gs.mult);
       const int64_t r = r0 + 32 * wv + 2 * (4 * i + j) + s;
+      // group of this lane's columns, and the packed word of the tile row (GRAN 32)
+      const int64_t g = (c0 + 8 * c) / GRAN;
+      uint32_t word = 0;
+      if constexpr (PACKED && GRAN == 32) {
+        word = ((c & 3) == 0 && g < G) ? gs.e8 << (8 * ((c >> 2) & 3)) : 0u;
+        word = group_or_u32<16>(word);
+      }
       if (r < rows) {
         if (validf == 8) {
           *reinterpret_cast<uint2 *>(q + r * q_ld + fc) = make_uint2(w0, w1);
@@ -529,7 +559,13 @@ __global__ __launch_bounds__(kThreads) void cast_dual_kernel(
           for (int e = 0; e < 8; ++e)
             if (e < validf) qp[e] = (uint8_t)((((e < 4) ? w0 : w1) >> (8 * (e & 3))) & 0xFFu);
         }
-        if (c == 0) sf[r * sf_s_row + (c0 >> 7) * sf_s_grp] = gs.sf;
+        if constexpr (!PACKED) {
+          if ((c & (GRAN / 8 - 1)) == 0 && g < G) store_scale<FMT>(sf, r * sf_s_row + g * sf_s_grp, gs);
+        } else if constexpr (GRAN == 32) {
+          if (c == 0) reinterpret_cast<uint32_t *>(sf)[r * sf_s_row + (c0 >> 7) * sf_s_grp] = word;
+        } else {
+          if (c == 0) store_packed_byte(sf, r * sf_s_row, sf_s_grp, c0 >> 7, G, gs.e8);
+        }
       }
     }
 
@@ -546,7 +582,7 @@ __global__ __launch_bounds__(kThreads) void cast_dual_kernel(
   }
   __syncthreads();
 
-  // columns: one 128-row group per tile column
+  // columns: 1 x GRAN groups along the tile column (4 lanes x 32 rows, or one lane's 32)
   const int p = t & 3;
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
@@ -566,13 +602,19 @@ __global__ __launch_bounds__(kThreads) void cast_dual_kernel(
     uint32_t am = 0;
 #pragma unroll
     for (int e = 0; e < 32; ++e) am = max(am, abs_bits(v[e]));
-    am = group_max_u32<4>(am);
+    if constexpr (GRAN == 128) am = group_max_u32<4>(am);
     const GroupScale gs = group_scale<UE8M0>(__uint_as_float(am));
     uint32_t o[8];
 #pragma unroll
     for (int m = 0; m < 8; ++m)
       o[m] = e4m3x4(v[4 * m] * gs.mult, v[4 * m + 1] * gs.mult, v[4 * m + 2] * gs.mult, v[4 * m + 3] * gs.mult);
     const int64_t f = c0 + fl, tk = r0 + 32 * p;
+    const int64_t gt = tk / GRAN;   // this thread's token group (GRAN 32), or the tile's (GRAN 128)
+    uint32_t word = 0;
+    if constexpr (PACKED && GRAN == 32) {
+      word = gt < GT ? gs.e8 << (8 * p) : 0u;
+      word = group_or_u32<4>(word);
+    }
     if (f < cols) {
       if (tk < rows) {
         uint8_t *qp = qT + f * qT_ld + tk;
@@ -586,7 +628,13 @@ __global__ __launch_bounds__(kThreads) void cast_dual_kernel(
             if (e < valid) qp[e] = (uint8_t)((o[e >> 2] >> (8 * (e & 3))) & 0xFFu);
         }
       }
-      if (p == 0) sfT[f * sfT_s_row + (r0 >> 7) * sfT_s_grp] = gs.sf;
+      if constexpr (!PACKED) {
+        if ((GRAN == 32 || p == 0) && gt < GT) store_scale<FMT>(sfT, f * sfT_s_row + gt * sfT_s_grp, gs);
+      } else if constexpr (GRAN == 32) {
+        if (p == 0) reinterpret_cast<uint32_t *>(sfT)[f * sfT_s_row + (r0 >> 7) * sfT_s_grp] = word;
+      } else {
+        if (p == 0) store_packed_byte(sfT, f * sfT_s_row, sfT_s_grp, r0 >> 7, GT, gs.e8);
+      }
     }
   }
 }
@@ -679,15 +727,20 @@ hipError_t launch_cast_dual(const CastDualArgs &a, hipStream_t st) {
   const int64_t tiles_c = (a.cols + 127) / 128, tiles = tiles_c * ((a.rows + 127) / 128);
   const dim3 grid((unsigned)tiles);
   const uint16_t *x = reinterpret_cast<const uint16_t *>(a.x);
-  float *sf = reinterpret_cast<float *>(a.sf), *sfT = reinterpret_cast<float *>(a.sfT);
-  if (a.sf_fmt == kSfUe8m0)
-    hipLaunchKernelGGL(cast_dual_kernel<true>, grid, dim3(kThreads), 0, st, x, a.rows, a.cols, a.x_ld, tiles_c,
-                       a.q, a.q_ld, sf, a.sf_stride_row, a.sf_stride_group, a.qT, a.qT_ld, sfT,
-                       a.sfT_stride_row, a.sfT_stride_group);
-  else
-    hipLaunchKernelGGL(cast_dual_kernel<false>, grid, dim3(kThreads), 0, st, x, a.rows, a.cols, a.x_ld, tiles_c,
-                       a.q, a.q_ld, sf, a.sf_stride_row, a.sf_stride_group, a.qT, a.qT_ld, sfT,
-                       a.sfT_stride_row, a.sfT_stride_group);
+#define FGFP8_DUAL(GR, F)                                                                                    \
+  hipLaunchKernelGGL((cast_dual_kernel<GR, F>), grid, dim3(kThreads), 0, st, x, a.rows, a.cols, a.x_ld, tiles_c, \
+                     a.q, a.q_ld, a.sf, a.sf_stride_row, a.sf_stride_group, a.qT, a.qT_ld, a.sfT,              \
+                     a.sfT_stride_row, a.sfT_stride_group)
+  if (a.gran_k == 32) {
+    if (a.sf_fmt == kSfPackedUe8m0) FGFP8_DUAL(32, kSfPackedUe8m0);
+    else if (a.sf_fmt == kSfUe8m0) FGFP8_DUAL(32, kSfUe8m0);
+    else FGFP8_DUAL(32, kSfFp32);
+  } else {
+    if (a.sf_fmt == kSfPackedUe8m0) FGFP8_DUAL(128, kSfPackedUe8m0);
+    else if (a.sf_fmt == kSfUe8m0) FGFP8_DUAL(128, kSfUe8m0);
+    else FGFP8_DUAL(128, kSfFp32);
+  }
+#undef FGFP8_DUAL
   return hipGetLastError();
 }
 

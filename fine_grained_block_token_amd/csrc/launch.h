@@ -40,7 +40,7 @@ struct CastBlockArgs {
 struct CastDualArgs {
   const void *x;
   int64_t rows, cols, x_ld;
-  int sf_fmt;
+  int gran_k, sf_fmt;
   uint8_t *q;
   int64_t q_ld;
   void *sf;

@@ -120,29 +120,35 @@ int cast_per_block(const void *x, int x_dtype, int64_t rows, int64_t cols, int64
 
 /*
  * cast_per_token_dual -- both per-token casts of one bf16 matrix from a single
- * read: the row-wise cast of x [rows, cols] (1 x 128 groups along cols) and
- * the row-wise cast of its transpose x^T [cols, rows] (1 x 128 groups along
+ * read: the row-wise cast of x [rows, cols] (1 x gran_k groups along cols) and
+ * the row-wise cast of its transpose x^T [cols, rows] (1 x gran_k groups along
  * rows).  Each output is bit-identical to the corresponding cast_per_token
- * call with gran_k = 128 (on x, and on the transposed view of x).  In an FP8
- * linear layer the first feeds the forward (or dgrad) GEMM and the second the
- * weight-gradient GEMM, whose K runs over tokens: "[Help] Starter script for
- * nn.Linear for fwd,bwd" (the wgrad line of the maintainer's pseudo-code) and
- * "DeepGEMM Essentials", Part 3 (the group rule).
+ * call with the same gran_k and sf_fmt (on x, and on the transposed view of
+ * x).  In an FP8 linear layer the first feeds the forward (or dgrad) GEMM and
+ * the second the weight-gradient GEMM, whose K runs over tokens: "[Help]
+ * Starter script for nn.Linear for fwd,bwd" (the wgrad line of the
+ * maintainer's pseudo-code) and "DeepGEMM Essentials", Part 3 (the group
+ * rule); group 32 and the scale formats as in "deep-gemm: fused per-token FP8
+ * cast in Triton".  With gran_k = 32 and packed scales it also casts a weight
+ * W for the group-32 recipe: q feeds the forward GEMM, qT the dgrad GEMM.
  *
  * x        bf16 [rows, cols] row-major, x_ld >= cols and a multiple of 8
  *          elements; 16-byte aligned.  x_dtype must be FGFP8_IN_BF16.
- * sf_fmt   FGFP8_SF_FP32 or FGFP8_SF_UE8M0 (packed UE8M0 is not offered here).
+ * gran_k   32 or 128.
+ * sf_fmt   FGFP8_SF_FP32, FGFP8_SF_UE8M0 or FGFP8_SF_PACKED_UE8M0.
  * q, sf    as cast_per_token on x: q [rows, cols] (8-byte aligned, q_ld >= cols,
  *          multiple of 8); sf float (r, g) at sf[r*sf_stride_row +
- *          g*sf_stride_group], g < ceil(cols/128), row-major or MN-major.
+ *          g*sf_stride_group], g < ceil(cols/gran_k), or packed int32 word
+ *          (r, w) at the same place, w < ceil(ceil(cols/gran_k)/4);
+ *          row-major or MN-major.
  * qT, sfT  as cast_per_token on x^T: qT [cols, rows] (16-byte aligned,
- *          qT_ld >= rows, multiple of 16); sfT float (c, g) at
- *          sfT[c*sfT_stride_row + g*sfT_stride_group], g < ceil(rows/128).
+ *          qT_ld >= rows, multiple of 16); sfT (c, g) or (c, w) at
+ *          sfT[c*sfT_stride_row + g*sfT_stride_group], g < ceil(rows/gran_k).
  * Writes exactly those elements.  rows == 0 or cols == 0: FGFP8_OK, nothing
  * launched.
  */
 int cast_per_token_dual(const void *x, int x_dtype, int64_t rows, int64_t cols, int64_t x_ld,
-                        int sf_fmt, uint8_t *q, int64_t q_ld,
+                        int gran_k, int sf_fmt, uint8_t *q, int64_t q_ld,
                         void *sf, int64_t sf_stride_row, int64_t sf_stride_group,
                         uint8_t *qT, int64_t qT_ld,
                         void *sfT, int64_t sfT_stride_row, int64_t sfT_stride_group,

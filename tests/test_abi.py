@@ -88,16 +88,17 @@ def test_cast_per_block_rejects(lib, kw):
 
 
 def dual(lib, **kw):
-    a = dict(x=P, dt=0, rows=256, cols=384, xld=384, fmt=0, q=Q, qld=384, sf=S, sfr=1, sfg=256,
+    a = dict(x=P, dt=0, rows=256, cols=384, xld=384, gran=128, fmt=0, q=Q, qld=384, sf=S, sfr=1, sfg=256,
              qT=Q, qTld=256, sfT=S, sfTr=1, sfTg=384, st=None)
     a.update(kw)
-    return lib.cast_per_token_dual(a["x"], a["dt"], a["rows"], a["cols"], a["xld"], a["fmt"], a["q"], a["qld"],
-                                   a["sf"], a["sfr"], a["sfg"], a["qT"], a["qTld"], a["sfT"], a["sfTr"],
+    return lib.cast_per_token_dual(a["x"], a["dt"], a["rows"], a["cols"], a["xld"], a["gran"], a["fmt"], a["q"],
+                                   a["qld"], a["sf"], a["sfr"], a["sfg"], a["qT"], a["qTld"], a["sfT"], a["sfTr"],
                                    a["sfTg"], a["st"])
 
 
 @pytest.mark.parametrize("kw", [
-    dict(dt=1), dict(fmt=2), dict(rows=-1), dict(x=None), dict(q=None), dict(sf=None), dict(qT=None),
+    dict(dt=1), dict(fmt=3), dict(gran=64), dict(gran=0), dict(fmt=2, gran=32, sfr=2, sfg=1),
+    dict(fmt=2, gran=32, sfTr=1, sfTg=1), dict(gran=32, sfr=11, sfg=1), dict(rows=-1), dict(x=None), dict(q=None), dict(sf=None), dict(qT=None),
     dict(sfT=None), dict(xld=380), dict(xld=388), dict(x=ctypes.c_void_p(0x10008)), dict(qld=380),
     dict(q=ctypes.c_void_p(0x20004)), dict(qTld=255), dict(qTld=264), dict(qT=ctypes.c_void_p(0x20008)),
     dict(sfg=255), dict(sfr=2, sfg=1), dict(sfTg=383), dict(sfTr=1, sfTg=1), dict(sf=ctypes.c_void_p(0x30002)),
@@ -107,7 +108,7 @@ def test_cast_per_token_dual_rejects(lib, kw):
 
 
 def test_cast_per_token_dual_zero_size_is_ok(lib):
-    assert dual(lib, rows=0) == 0 and dual(lib, cols=0) == 0
+    assert dual(lib, rows=0) == 0 and dual(lib, cols=0) == 0 and dual(lib, rows=0, gran=32, fmt=2) == 0
 
 
 def gemm(lib, **kw):

@@ -1,8 +1,9 @@
 """GPU parity of the dual-orientation per-token cast: one read of bf16 x gives
 q/sf bit-identical to the oracle's per-token cast of x and qT/sfT bit-identical
-to its per-token cast of x^T (1x128 groups; "DeepGEMM Essentials", Part 3, and
-the wgrad operands of "[Help] Starter script for nn.Linear for fwd,bwd").
-Writes must stay inside the given views."""
+to its per-token cast of x^T (1x128 or 1x32 groups, fp32 / UE8M0 / packed UE8M0
+scales; "DeepGEMM Essentials", Part 3, the wgrad operands of "[Help] Starter
+script for nn.Linear for fwd,bwd", and the group-32 formats of "deep-gemm:
+fused per-token FP8 cast in Triton").  Writes must stay inside the given views."""
 import numpy as np
 import pytest
 import torch
@@ -15,17 +16,19 @@ from gpu_util import oracle_sf_bits, say, sentinel_u8
 pytestmark = pytest.mark.gpu
 
 
-def _scale_view(rows, groups, mn_major, pad):
-    """fp32 scale view [rows, groups] over a sentinel-filled buffer; returns (view, buffer)."""
+def _scale_view(rows, groups, mn_major, pad, packed=False):
+    """Scale view [rows, groups] (float32, or int32 words when packed) over a sentinel-filled
+    buffer; returns (view, buffer)."""
+    dt = torch.int32 if packed else torch.float32
     if mn_major:
         ld = -(-(rows + pad) // 4) * 4
         buf = torch.full((groups, ld), -7, dtype=torch.int32, device="cuda")
-        return buf.view(torch.float32).t()[:rows], buf
+        return buf.view(dt).t()[:rows], buf
     buf = torch.full((rows, groups + pad), -7, dtype=torch.int32, device="cuda")
-    return buf.view(torch.float32)[:, :groups], buf
+    return buf.view(dt)[:, :groups], buf
 
 
-def _run_dual(x_cpu, fmt, mn_major=True):
+def _run_dual(x_cpu, fmt, mn_major=True, gran=128):
     rows, cols = x_cpu.shape
     x_ld = -(-cols // 8) * 8          # the kernel reads 16-byte chunks of each row
     xbuf = torch.zeros((rows, x_ld), dtype=torch.bfloat16, device="cuda")
@@ -35,11 +38,14 @@ def _run_dual(x_cpu, fmt, mn_major=True):
     qT_ld = -(-(rows + 16) // 16) * 16
     qbuf, qTbuf = sentinel_u8((rows, q_ld)), sentinel_u8((cols, qT_ld))
     q, qT = qbuf[:, :cols], qTbuf[:, :rows]
-    G, GT = fg.num_groups(cols, 128), fg.num_groups(rows, 128)
-    sf, sbuf = _scale_view(rows, G, mn_major, 4)
-    sfT, sTbuf = _scale_view(cols, GT, mn_major, 4)
-    say("cast_per_token_dual", (rows, cols), "fmt", fmt, "mn", mn_major)
-    fg.cast_per_token_dual(x, q, sf, qT, sfT, fmt)
+    packed = fmt == oracle.SF_PACKED_UE8M0
+    G, GT = fg.num_groups(cols, gran), fg.num_groups(rows, gran)
+    if packed:
+        G, GT = -(-G // 4), -(-GT // 4)   # words of four groups
+    sf, sbuf = _scale_view(rows, G, mn_major, 4, packed)
+    sfT, sTbuf = _scale_view(cols, GT, mn_major, 4, packed)
+    say("cast_per_token_dual", (rows, cols), "gran", gran, "fmt", fmt, "mn", mn_major)
+    fg.cast_per_token_dual(x, q, sf, qT, sfT, fmt, gran)
     torch.cuda.synchronize()
     got = (q.cpu().numpy(), sf.contiguous().view(torch.int32).cpu().numpy().view(np.uint32),
            qT.cpu().numpy(), sfT.contiguous().view(torch.int32).cpu().numpy().view(np.uint32))
@@ -52,10 +58,10 @@ def _run_dual(x_cpu, fmt, mn_major=True):
     return got
 
 
-def _check(x_cpu, fmt, mn_major=True):
-    q, sf, qT, sfT = _run_dual(x_cpu, fmt, mn_major)
-    oq, osf = oracle.cast_per_token(si.host_array(x_cpu), 128, fmt)
-    oqT, osfT = oracle.cast_per_token(si.host_array(x_cpu), 128, fmt, transpose=True)
+def _check(x_cpu, fmt, mn_major=True, gran=128):
+    q, sf, qT, sfT = _run_dual(x_cpu, fmt, mn_major, gran)
+    oq, osf = oracle.cast_per_token(si.host_array(x_cpu), gran, fmt)
+    oqT, osfT = oracle.cast_per_token(si.host_array(x_cpu), gran, fmt, transpose=True)
     assert np.array_equal(q, oq), "row-wise E4M3 bytes differ"
     assert np.array_equal(sf, oracle_sf_bits(osf)), "row-wise scale bits differ"
     assert np.array_equal(qT, oqT), "transposed E4M3 bytes differ"
@@ -70,15 +76,39 @@ def test_dual_matches_both_casts(gpu, shape, fmt):
     _check(si.cast_workload(*shape, seed=si.SEED_A), fmt, mn_major=True)
 
 
+@pytest.mark.parametrize("shape", [(1, 512), (7, 4096), (129, 7168), (64, 1000), (128, 128), (129, 257),
+                                   (200, 300), (5, 3), (640, 96), (300, 1000)])
+@pytest.mark.parametrize("fmt", [oracle.SF_FP32, oracle.SF_UE8M0, oracle.SF_PACKED_UE8M0],
+                         ids=["fp32", "ue8m0", "packed"])
+def test_dual_group32(gpu, shape, fmt):
+    _check(si.cast_workload(*shape, seed=si.SEED_A), fmt, mn_major=True, gran=32)
+
+
+@pytest.mark.parametrize("shape", [(1, 512), (129, 7168), (64, 1000), (200, 300), (5, 3), (640, 96), (700, 1300)])
+def test_dual_group128_packed(gpu, shape):
+    # one packed word spans four 128-column tiles: each tile stores its own byte
+    _check(si.cast_workload(*shape, seed=si.SEED_B), oracle.SF_PACKED_UE8M0, mn_major=True, gran=128)
+
+
 @pytest.mark.parametrize("shape", [(300, 200), (1000, 64)])
-def test_dual_row_major_scales(gpu, shape):
-    _check(si.cast_workload(*shape, seed=si.SEED_B), oracle.SF_FP32, mn_major=False)
+@pytest.mark.parametrize("gran_fmt", [(128, oracle.SF_FP32), (32, oracle.SF_FP32), (32, oracle.SF_PACKED_UE8M0),
+                                      (128, oracle.SF_PACKED_UE8M0)], ids=["g128", "g32", "g32packed", "g128packed"])
+def test_dual_row_major_scales(gpu, shape, gran_fmt):
+    gran, fmt = gran_fmt
+    _check(si.cast_workload(*shape, seed=si.SEED_B), fmt, mn_major=False, gran=gran)
 
 
 @pytest.mark.parametrize("shape", [(8192, 7168), (8192, 4096)], ids=["x", "dY"])
 def test_dual_linear_operands(gpu, shape):
     # the linear step's x [tokens, in] and dY [tokens, out] at full size
     _check(si.randn(shape, si.SEED_A if shape[1] == 7168 else si.SEED_DY), oracle.SF_FP32, mn_major=True)
+
+
+@pytest.mark.parametrize("shape", [(8192, 7168), (4096, 7168)], ids=["x", "W"])
+def test_dual_group32_packed_linear_operands(gpu, shape):
+    # the group-32 recipe's x (and x^T), and W (and W^T), at full size
+    _check(si.randn(shape, si.SEED_A if shape[0] == 8192 else si.SEED_B), oracle.SF_PACKED_UE8M0, mn_major=True,
+           gran=32)
 
 
 def test_dual_zero_size_is_noop(gpu):
