@@ -310,6 +310,8 @@ def extra_kernels(fg, torch, si):
     for scale in (1, 32):
         tokens = [t * scale for t in si.MOE_TOKENS_8]
         out[f"m_grouped_8experts_tokens{sum(tokens)}_hidden2048"] = grouped_gemm_rate(fg, torch, si, tokens, 2048, 2048)
+        out[f"m_grouped_ue8m0_g32_8experts_tokens{sum(tokens)}_hidden2048"] = grouped_gemm_g32_rate(
+            fg, torch, si, tokens, 2048, 2048)
     return out
 
 
@@ -348,6 +350,28 @@ def grouped_gemm_rate(fg, torch, si, tokens, n, k):
     torch.cuda.synchronize()
     r = _measure(torch, "TFLOPS", 2.0 * sum(tokens) * n * k,
                  lambda: fg.m_grouped_gemm_fp8_nt_bf16_contiguous(A, sa, B, sb, m_idx, D))
+    r["rows_with_padding"] = m
+    return r
+
+
+def grouped_gemm_g32_rate(fg, torch, si, tokens, n, k):
+    """As grouped_gemm_rate, in the UE8M0 group-32 recipe (A and every expert's B cast per
+    row with 32-wide groups and packed scales)."""
+    m_idx = torch.from_numpy(si.grouped_layout(tokens)).cuda()
+    m, E = m_idx.numel(), len(tokens)
+    a = si.randn((m, k), si.SEED_A, 0.1).cuda()
+    A = torch.empty((m, k), dtype=torch.uint8, device="cuda")
+    sa = fg.mn_major_scales(m, k // 128, torch.int32)
+    fg.cast_per_token(a, A, sa, 32, fg.SF_PACKED_UE8M0)
+    B = torch.empty((E, n, k), dtype=torch.uint8, device="cuda")
+    ld = -(-n // 4) * 4
+    sb = torch.empty((E, k // 128, ld), dtype=torch.int32, device="cuda").permute(0, 2, 1)[:, :n]
+    for e in range(E):
+        fg.cast_per_token(si.randn((n, k), si.SEED_B + e, 0.1).cuda(), B[e], sb[e], 32, fg.SF_PACKED_UE8M0)
+    D = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    torch.cuda.synchronize()
+    r = _measure(torch, "TFLOPS", 2.0 * sum(tokens) * n * k,
+                 lambda: fg.m_grouped_gemm_fp8_nt_bf16_ue8m0_g32_contiguous(A, sa, B, sb, m_idx, D))
     r["rows_with_padding"] = m
     return r
 

@@ -48,11 +48,14 @@ def load():
                                           i64, i64, i64, p]
     lib.gemm_fp8_nt_bf16_ue8m0_g32.argtypes = [p, i64, p, i64, p, i64, p, i64, p, i64, i64, i64, i64, p]
     lib.wgrad_gemm_fp8_nt_fp32_ue8m0_g32.argtypes = [p, i64, p, i64, p, i64, p, i64, p, i64, i64, i64, i64, p]
+    lib.m_grouped_gemm_fp8_nt_bf16_ue8m0_g32_contiguous.argtypes = [p, i64, p, i64, p, i64, i64, p, i64, i64, p, i64,
+                                                                    p, i64, i64, i64, i64, p]
     lib.m_grouped_gemm_fp8_nt_bf16_contiguous.argtypes = [p, i64, p, i32, i64, p, i64, i64, p, i64, i64, p, i64,
                                                           p, i64, i64, i64, i64, p]
     for f in ("cast_per_token", "cast_per_block", "cast_per_token_dual", "gemm_fp8_nt_bf16",
               "wgrad_gemm_fp8_nt_fp32", "m_grouped_gemm_fp8_nt_bf16_contiguous", "gemm_fp8_nt_bf16_cast",
-              "gemm_fp8_nt_bf16_ue8m0_g32", "wgrad_gemm_fp8_nt_fp32_ue8m0_g32"):
+              "gemm_fp8_nt_bf16_ue8m0_g32", "wgrad_gemm_fp8_nt_fp32_ue8m0_g32",
+              "m_grouped_gemm_fp8_nt_bf16_ue8m0_g32_contiguous"):
         getattr(lib, f).restype = i32
     lib.fgfp8_status_string.argtypes = [i32]
     lib.fgfp8_status_string.restype = ctypes.c_char_p
@@ -62,7 +65,8 @@ def load():
 
 EXPORTED = ("cast_per_token", "cast_per_block", "cast_per_token_dual", "gemm_fp8_nt_bf16",
             "wgrad_gemm_fp8_nt_fp32", "m_grouped_gemm_fp8_nt_bf16_contiguous", "gemm_fp8_nt_bf16_cast",
-            "gemm_fp8_nt_bf16_ue8m0_g32", "wgrad_gemm_fp8_nt_fp32_ue8m0_g32", "fgfp8_status_string")
+            "gemm_fp8_nt_bf16_ue8m0_g32", "wgrad_gemm_fp8_nt_fp32_ue8m0_g32",
+            "m_grouped_gemm_fp8_nt_bf16_ue8m0_g32_contiguous", "fgfp8_status_string")
 
 
 def _check(rc: int, what: str):
@@ -236,6 +240,27 @@ def m_grouped_gemm_fp8_nt_bf16_contiguous(A: torch.Tensor, sa: torch.Tensor, B: 
         _ptr(A), A.stride(0), _ptr(sa), sa_fmt, sa_ld, _ptr(B), B.stride(1), B.stride(0), _ptr(sb), sb.stride(1),
         sb.stride(0), _ptr(m_indices), E, _ptr(D), D.stride(0), m, n, k, _stream(A)),
         "m_grouped_gemm_fp8_nt_bf16_contiguous")
+
+
+def m_grouped_gemm_fp8_nt_bf16_ue8m0_g32_contiguous(A: torch.Tensor, sa: torch.Tensor, B: torch.Tensor,
+                                                    sb: torch.Tensor, m_indices: torch.Tensor,
+                                                    D: torch.Tensor) -> None:
+    """m-grouped contiguous GEMM in the UE8M0 group-32 recipe: row i of D (bf16 [m, n]) =
+    (A[i]*sa[i]) (B[e]*sb[e])^T, e = m_indices[i] (int32, -1 = padding row, not written).
+    A, sa as gemm_fp8_nt_bf16_ue8m0_g32; B [E, n, k] E4M3; sb [E, n, k/128] int32 packed words with
+    stride(1) == 1: expert e's word (j, kb) at sb[e] offset kb*stride(2) + j."""
+    A, B = _u8(A), _u8(B)
+    m, k = A.shape
+    E, n = B.shape[0], B.shape[1]
+    if sa.shape[0] > 1 and sa.stride(0) != 1:
+        raise ValueError("sa must be MN-major (stride(0) == 1)")
+    if sb.dim() != 3 or (sb.shape[1] > 1 and sb.stride(1) != 1):
+        raise ValueError("sb must be [E, n, k/128] with each expert's words MN-major (stride(1) == 1)")
+    sa_ld = sa.stride(1) if sa.dim() == 2 else m
+    _check(load().m_grouped_gemm_fp8_nt_bf16_ue8m0_g32_contiguous(
+        _ptr(A), A.stride(0), _ptr(sa), sa_ld, _ptr(B), B.stride(1), B.stride(0), _ptr(sb), sb.stride(2),
+        sb.stride(0), _ptr(m_indices), E, _ptr(D), D.stride(0), m, n, k, _stream(A)),
+        "m_grouped_gemm_fp8_nt_bf16_ue8m0_g32_contiguous")
 
 
 def wgrad_gemm_fp8_nt_fp32(A: torch.Tensor, sa: torch.Tensor, B: torch.Tensor, sb: torch.Tensor,

@@ -216,6 +216,30 @@ int wgrad_gemm_fp8_nt_fp32_ue8m0_g32(const uint8_t *A, int64_t lda, const uint32
   return launched(fgfp8::launch_gemm_g32(a, static_cast<hipStream_t>(stream)));
 }
 
+int m_grouped_gemm_fp8_nt_bf16_ue8m0_g32_contiguous(const uint8_t *A, int64_t lda, const uint32_t *sa,
+                                                    int64_t sa_ld, const uint8_t *B, int64_t ldb,
+                                                    int64_t b_expert_stride, const uint32_t *sb, int64_t sb_ld,
+                                                    int64_t sb_expert_stride, const int32_t *m_indices,
+                                                    int64_t num_experts, uint16_t *D, int64_t ldd, int64_t m,
+                                                    int64_t n, int64_t k, void *stream) {
+  const int c = check_gemm_common(A, lda, sa, sa_ld, B, ldb, reinterpret_cast<const float *>(sb), D, m, n, k);
+  if (c != 1) return c;
+  if (sb_ld < n) return FGFP8_EINVAL;
+  if (!aligned(D, 16) || ldd < n || ldd % 8 != 0) return FGFP8_EINVAL;
+  if (num_experts < 1 || num_experts > 0x7FFFFFFF || !m_indices || !aligned(m_indices, 4)) return FGFP8_EINVAL;
+  if (b_expert_stride < (n - 1) * ldb + k || b_expert_stride % 16 != 0) return FGFP8_EINVAL;
+  if (sb_expert_stride < (k / 128 - 1) * sb_ld + n) return FGFP8_EINVAL;
+  const int dev = check_device();
+  if (dev != FGFP8_OK) return dev;
+  fgfp8::GemmArgs a{A, lda, sa, kSfPackedUe8m0, sa_ld, B, ldb, reinterpret_cast<const float *>(sb), sb_ld,
+                    D, ldd, m, n, k, false};
+  a.m_idx = m_indices;
+  a.num_experts = num_experts;
+  a.b_estride = b_expert_stride;
+  a.sb_estride = sb_expert_stride;
+  return launched(fgfp8::launch_gemm_g32(a, static_cast<hipStream_t>(stream)));
+}
+
 int m_grouped_gemm_fp8_nt_bf16_contiguous(const uint8_t *A, int64_t lda, const void *sa, int sa_fmt,
                                           int64_t sa_ld, const uint8_t *B, int64_t ldb, int64_t b_expert_stride,
                                           const float *sb, int64_t sb_ld, int64_t sb_expert_stride,

@@ -440,7 +440,7 @@ __device__ __forceinline__ v8i frag_g32(const uint8_t *tile, int row, int lane) 
   return r;
 }
 
-template <class C, bool WGRAD>
+template <class C, bool WGRAD, bool GROUPED>
 __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_g32_kernel(GemmArgs g, int tiles_m, int tiles_n) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::kStages * C::kStageBytes];
   const int t = threadIdx.x, lane = t & 63;
@@ -458,6 +458,23 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_g32_kernel(Ge
   const int64_t m0 = (int64_t)tm * C::kBM, n0 = (int64_t)tn * C::kBN;
   const int64_t m = g.m, n = g.n;
   const int KB = (int)(g.k / kBK);
+
+  // m-grouped layout (as in gemm_kernel): the tile's rows belong to the expert with
+  // the largest m_indices among them; a tile without a valid expert returns whole.
+  const uint8_t *Bg = g.B;
+  const uint32_t *sbw = reinterpret_cast<const uint32_t *>(g.sb);
+  int expert = 0;
+  if constexpr (GROUPED) {
+    static_assert(C::kBM == 128, "one 128-row segment block per tile");
+    uint32_t v = 0;
+#pragma unroll
+    for (int r = 0; r < C::kBM; r += 64)
+      if (m0 + r + lane < m) v = max(v, (uint32_t)(g.m_idx[m0 + r + lane] + 1));
+    expert = (int)wave_max_u32(v) - 1;
+    if (expert < 0 || expert >= g.num_experts) return;
+    Bg = g.B + (int64_t)expert * g.b_estride;
+    sbw += (int64_t)expert * g.sb_estride;
+  }
 
   uint32_t a_off[C::kALoads], b_off[C::kBLoads];
 #pragma unroll
@@ -477,10 +494,9 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_g32_kernel(Ge
   const uint32_t scale_off = sa_loader ? 4u * (uint32_t)min((int64_t)(64 * wv + lane), m - 1 - m0)
                                        : 4u * (uint32_t)min((int64_t)(64 * (wv - C::kSaLoads) + lane), n - 1 - n0);
   const uint32_t *saw = reinterpret_cast<const uint32_t *>(g.sa);
-  const uint32_t *sbw = reinterpret_cast<const uint32_t *>(g.sb);
   auto issue = [&](int kb, uint8_t *st) {
     const uint8_t *ga = g.A + m0 * g.lda + (int64_t)kb * kBK;
-    const uint8_t *gb = g.B + n0 * g.ldb + (int64_t)kb * kBK;
+    const uint8_t *gb = Bg + n0 * g.ldb + (int64_t)kb * kBK;
 #pragma unroll
     for (int i = 0; i < C::kALoads; ++i) load_lds16(ga, a_off[i], st + 1024 * (i * C::kWaves + wv));
 #pragma unroll
@@ -527,6 +543,9 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_g32_kernel(Ge
   for (int mi = 0; mi < 4; ++mi) {
     const int64_t i = m0 + wm + 16 * mi + (lane & 15);
     if (i >= m) continue;
+    if constexpr (GROUPED) {
+      if (g.m_idx[i] != expert) continue;   // padding (or another expert's) row
+    }
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni) {
       const int64_t j = n0 + wn + 16 * ni + 4 * (lane >> 4);
@@ -726,12 +745,13 @@ hipError_t launch_gemm_g32(const GemmArgs &a, hipStream_t st) {
   using C = Cfg<2, 2, 2>;
   const int tiles_m = (int)((a.m + C::kBM - 1) / C::kBM), tiles_n = (int)((a.n + C::kBN - 1) / C::kBN);
   const int per_xcd = (tiles_m * tiles_n + kXcds - 1) / kXcds;
+  const dim3 grid((unsigned)(per_xcd * kXcds));
   if (a.wgrad)
-    hipLaunchKernelGGL((gemm_g32_kernel<C, true>), dim3((unsigned)(per_xcd * kXcds)), dim3(C::kThreads), 0, st, a,
-                       tiles_m, tiles_n);
+    hipLaunchKernelGGL((gemm_g32_kernel<C, true, false>), grid, dim3(C::kThreads), 0, st, a, tiles_m, tiles_n);
+  else if (a.m_idx != nullptr)
+    hipLaunchKernelGGL((gemm_g32_kernel<C, false, true>), grid, dim3(C::kThreads), 0, st, a, tiles_m, tiles_n);
   else
-    hipLaunchKernelGGL((gemm_g32_kernel<C, false>), dim3((unsigned)(per_xcd * kXcds)), dim3(C::kThreads), 0, st, a,
-                       tiles_m, tiles_n);
+    hipLaunchKernelGGL((gemm_g32_kernel<C, false, false>), grid, dim3(C::kThreads), 0, st, a, tiles_m, tiles_n);
   return hipGetLastError();
 }
 

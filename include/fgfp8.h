@@ -281,6 +281,31 @@ int m_grouped_gemm_fp8_nt_bf16_contiguous(const uint8_t *A, int64_t lda, const v
                                           int64_t n, int64_t k, void *stream);
 
 /*
+ * m_grouped_gemm_fp8_nt_bf16_ue8m0_g32_contiguous -- the m-grouped contiguous
+ * GEMM of m_grouped_gemm_fp8_nt_bf16_contiguous in the UE8M0 group-32 recipe
+ * (the packed-UE8M0 group-32 scales that "deep-gemm: fused per-token FP8 cast
+ * in Triton" names for MoE): row i with m_indices[i] = e >= 0 gets
+ *     D[i, :] = (A[i] * sa[i]) (B_e * sb_e)^T,
+ * computed exactly as gemm_fp8_nt_bf16_ue8m0_g32 computes a row.
+ *
+ * A, sa, sa_ld, D, ldd, m, n, k   as gemm_fp8_nt_bf16_ue8m0_g32 (m = all rows,
+ *          padding included).
+ * B        expert e's E4M3 [n, k] at B + e*b_expert_stride (bytes), as in
+ *          m_grouped_gemm_fp8_nt_bf16_contiguous.
+ * sb       expert e's packed words at sb + e*sb_expert_stride (int32 words),
+ *          (j, kb) at [kb*sb_ld + j], sb_ld >= n; sb_expert_stride >=
+ *          (k/128 - 1)*sb_ld + n.
+ * m_indices, num_experts and the layout requirement as in
+ *          m_grouped_gemm_fp8_nt_bf16_contiguous.
+ */
+int m_grouped_gemm_fp8_nt_bf16_ue8m0_g32_contiguous(const uint8_t *A, int64_t lda, const uint32_t *sa,
+                                                    int64_t sa_ld, const uint8_t *B, int64_t ldb,
+                                                    int64_t b_expert_stride, const uint32_t *sb, int64_t sb_ld,
+                                                    int64_t sb_expert_stride, const int32_t *m_indices,
+                                                    int64_t num_experts, uint16_t *D, int64_t ldd, int64_t m,
+                                                    int64_t n, int64_t k, void *stream);
+
+/*
  * wgrad_gemm_fp8_nt_fp32 -- D += (A * sa)(B * sb)^T in fp32 (weight gradient).
  * Defined by "DeepGEMM Essentials", Parts 12-13 (the weight gradient is
  * accumulated into an existing fp32 tensor, expected = original + dY^T x)

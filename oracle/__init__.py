@@ -295,6 +295,38 @@ def gemm_nt_g32(A, sa, B, sb, idx=None):
     return np.einsum("ij,ij->i", a[ii], b[jj]), np.einsum("ij,ij->i", np.abs(a[ii]), np.abs(b[jj]))
 
 
+def m_grouped_gemm_nt_g32(A, sa, B, sb, m_indices, idx=None):
+    """fp64 reference of the m-grouped contiguous GEMM ("DeepGEMM Essentials",
+    Parts 8-11) in the group-32 recipe: row i uses expert e = m_indices[i] and
+    gives D[i] = gemm_nt_g32 of (A[i], sa[i]) with (B[e], sb[e]); padding rows
+    (m_indices[i] == -1) have no reference (NaN).
+
+    A uint8 [m, k]; sa float32 [m, k/32]; B uint8 [E, n, k]; sb float32
+    [E, n, k/32]; m_indices int [m].  Returns (ref, absum) like gemm_nt.
+    """
+    B = np.asarray(B)
+    sb = np.asarray(sb)
+    e_of = np.asarray(m_indices, dtype=np.int64)
+    m, n = np.shape(A)[0], B.shape[1]
+    if idx is None:
+        ref = np.full((m, n), np.nan)
+        absum = np.full((m, n), np.nan)
+        for e in range(B.shape[0]):
+            rows = np.nonzero(e_of == e)[0]
+            if rows.size:
+                ref[rows], absum[rows] = gemm_nt_g32(np.asarray(A)[rows], np.asarray(sa)[rows], B[e], sb[e])
+        return ref, absum
+    ii = np.asarray(idx[0], dtype=np.int64)
+    jj = np.asarray(idx[1], dtype=np.int64)
+    ref = np.full(ii.size, np.nan)
+    absum = np.full(ii.size, np.nan)
+    for e in range(B.shape[0]):
+        sel = np.nonzero(e_of[ii] == e)[0]
+        if sel.size:
+            ref[sel], absum[sel] = gemm_nt_g32(A, sa, B[e], sb[e], idx=(ii[sel], jj[sel]))
+    return ref, absum
+
+
 def wgrad_nt_g32(A, sa, B, sb, d_in, idx=None):
     """Weight-gradient form of gemm_nt_g32 ("DeepGEMM Essentials", Parts 12-13: K
     runs over tokens and the fp32 output is accumulated): D_in + gemm_nt_g32.

@@ -27,7 +27,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for f in ("cast_per_token", "cast_per_block", "cast_per_token_dual", "gemm_fp8_nt_bf16",
               "wgrad_gemm_fp8_nt_fp32", "m_grouped_gemm_fp8_nt_bf16_contiguous", "gemm_fp8_nt_bf16_cast",
-              "gemm_fp8_nt_bf16_ue8m0_g32", "wgrad_gemm_fp8_nt_fp32_ue8m0_g32", "fgfp8_status_string"):
+              "gemm_fp8_nt_bf16_ue8m0_g32", "wgrad_gemm_fp8_nt_fp32_ue8m0_g32",
+              "m_grouped_gemm_fp8_nt_bf16_ue8m0_g32_contiguous", "fgfp8_status_string"):
         assert f in names
 
 
@@ -221,3 +222,27 @@ def test_wgrad_g32_rejects(lib, kw):
 
 def test_wgrad_g32_zero_size_is_ok(lib):
     assert wg32(lib, m=0) == 0 and wg32(lib, n=0) == 0
+
+
+MI = ctypes.c_void_p(0x40000)
+
+
+def gg32(lib, **kw):
+    a = dict(A=P, lda=256, sa=S, sald=384, B=Q, ldb=256, bes=256 * 256, sb=S, sbld=256, sbes=512, mi=MI, ne=4,
+             D=P, ldd=256, m=384, n=256, k=256, st=None)
+    a.update(kw)
+    return lib.m_grouped_gemm_fp8_nt_bf16_ue8m0_g32_contiguous(
+        a["A"], a["lda"], a["sa"], a["sald"], a["B"], a["ldb"], a["bes"], a["sb"], a["sbld"], a["sbes"], a["mi"],
+        a["ne"], a["D"], a["ldd"], a["m"], a["n"], a["k"], a["st"])
+
+
+@pytest.mark.parametrize("kw", [dict(sbld=255), dict(sald=383), dict(k=96), dict(sb=None), dict(mi=None),
+                                dict(mi=ctypes.c_void_p(0x40002)), dict(ne=0), dict(bes=256 * 256 - 1),
+                                dict(bes=256 * 255 + 256 + 8), dict(sbes=511), dict(ldd=252),
+                                dict(D=ctypes.c_void_p(0x10008))])
+def test_grouped_g32_rejects(lib, kw):
+    assert gg32(lib, **kw) == -1
+
+
+def test_grouped_g32_zero_size_is_ok(lib):
+    assert gg32(lib, m=0) == 0 and gg32(lib, n=0) == 0

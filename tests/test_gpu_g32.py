@@ -161,3 +161,57 @@ def test_wgrad_g32_linear_size_sampled(gpu):
     ref, absum = oracle.wgrad_nt_g32(qa, sa, qb, sb, zero, idx=(ii, jj))
     tb = mfma_truncation_bound(qa, sa, qb, sb, sb_block=False, idx=(ii, jj), group=32)
     _check_wgrad(got[ii, jj], ref, absum, tb, tokens, "wgrad g32 4096x7168x8192")
+
+
+# m-grouped contiguous GEMM in the group-32 recipe: rows of expert e use B[e] and its
+# per-row group-32 scales; padding rows (-1) must stay untouched.
+
+def _grouped_operands(m_idx, E, n, k, seed):
+    m = m_idx.size
+    qa, wa = oracle.cast_per_token(si.host_array(si.randn((m, k), seed, 0.1)), 32, oracle.SF_PACKED_UE8M0)
+    qb = np.empty((E, n, k), np.uint8)
+    wb = np.empty((E, n, k // 128), np.uint32)
+    for e in range(E):
+        qb[e], wb[e] = oracle.cast_per_token(si.host_array(si.randn((n, k), seed + 1 + e, 0.1)), 32,
+                                             oracle.SF_PACKED_UE8M0)
+    return qa, wa, qb, wb
+
+
+def _run_grouped(qa, wa, qb, wb, m_idx):
+    m, k = qa.shape
+    E, n = qb.shape[0], qb.shape[1]
+    ld = -(-n // 4) * 4 + 4
+    sb = torch.zeros((E, k // 128, ld), dtype=torch.int32)
+    sb[:, :, :n] = torch.from_numpy(np.ascontiguousarray(wb.transpose(0, 2, 1)).view(np.int32))
+    sb = sb.cuda().permute(0, 2, 1)[:, :n]
+    ldd = -(-n // 8) * 8
+    D = torch.full((m, ldd), 0x7FC0, dtype=torch.int16, device="cuda")
+    say("m_grouped_gemm_fp8_nt_bf16_ue8m0_g32_contiguous", (m, n, k), "experts", E)
+    fg.m_grouped_gemm_fp8_nt_bf16_ue8m0_g32_contiguous(
+        torch.from_numpy(qa).cuda(), _dev_words(wa), torch.from_numpy(qb).cuda(), sb,
+        torch.from_numpy(m_idx).cuda(), D[:, :n].view(torch.bfloat16))
+    torch.cuda.synchronize()
+    Dh = D.cpu().numpy().view(np.uint16)
+    assert (Dh[:, n:] == 0x7FC0).all()
+    return Dh[:, :n]
+
+
+@pytest.mark.parametrize("tokens,n,k", [(si.MOE_TOKENS_4, 256, 512), (si.MOE_TOKENS_8, 200, 384),
+                                        ([1, 300, 0, 129], 130, 256)])
+def test_grouped_g32_full_compare(gpu, tokens, n, k):
+    m_idx = si.grouped_layout(tokens)
+    E = len(tokens)
+    qa, wa, qb, wb = _grouped_operands(m_idx, E, n, k, seed=50)
+    got = _run_grouped(qa, wa, qb, wb, m_idx)
+    sa = oracle.unpack_ue8m0(wa, k // 32)
+    sb = np.stack([oracle.unpack_ue8m0(wb[e], k // 32) for e in range(E)])
+    ref, absum = oracle.m_grouped_gemm_nt_g32(qa, sa, qb, sb, m_idx)
+    pad = m_idx < 0
+    assert (got[pad] == 0x7FC0).all(), "padding rows were written"
+    valid = np.nonzero(~pad)[0]
+    tb = np.zeros((valid.size, n))
+    for e in range(E):
+        rows = np.nonzero(m_idx[valid] == e)[0]
+        if rows.size:
+            tb[rows] = mfma_truncation_bound(qa[valid[rows]], sa[valid[rows]], qb[e], sb[e], sb_block=False, group=32)
+    check_bf16_gemm(got[valid], ref[valid], absum[valid], tb, k // 8, f"grouped g32 {tokens}")

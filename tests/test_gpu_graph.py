@@ -47,6 +47,9 @@ def test_graph_replays_match_eager(gpu):
     Wgq = torch.empty((E, O, I), dtype=u8, device="cuda")
     sWg = torch.empty((E, O // 128, I // 128), dtype=f32, device="cuda")
     yg = torch.empty((m_idx.numel(), O), dtype=torch.bfloat16, device="cuda")
+    Wg32 = torch.empty((E, O, I), dtype=u8, device="cuda")
+    sWg32 = torch.empty((E, I // 128, O), dtype=torch.int32, device="cuda").permute(0, 2, 1)
+    yg32 = torch.empty((m_idx.numel(), O), dtype=torch.bfloat16, device="cuda")
 
     def step():
         fg.cast_per_token(x, xq, sx, 128, fg.SF_FP32)
@@ -66,9 +69,12 @@ def test_graph_replays_match_eager(gpu):
         for e in range(E):
             fg.cast_per_block(Wg[e], Wgq[e], sWg[e], sf_fmt=fg.SF_FP32)
         fg.m_grouped_gemm_fp8_nt_bf16_contiguous(xq[:m_idx.numel()], sx[:m_idx.numel()], Wgq, sWg, m_idx, yg)
+        for e in range(E):
+            fg.cast_per_token(Wg[e], Wg32[e], sWg32[e], 32, fg.SF_PACKED_UE8M0)
+        fg.m_grouped_gemm_fp8_nt_bf16_ue8m0_g32_contiguous(wp, swp, Wg32, sWg32, m_idx, yg32)
 
     outs = [xq, sx, xq1, sx1, wp, swp, xTq, sxT, Wq, sW, y, y1, dq, dsx, dqT, dsxT, yq, ysf, y2, W32, sW32, y32,
-            xT32, sxT32, dW32, Wgq, sWg, yg]
+            xT32, sxT32, dW32, Wgq, sWg, yg, Wg32, yg32]
 
     def snap():
         return [o.cpu().clone() for o in outs], dW.cpu().clone()

@@ -85,3 +85,29 @@ def test_wgrad_g32_all_ones_closed_form_with_d_in():
     want = d_in.astype(np.float64) + np.array(
         [[sum(32 * 2.0 ** (ea[i, g] + eb[j, g]) for g in range(k // 32)) for j in range(n)] for i in range(m)])
     assert np.array_equal(ref, want)
+
+
+def test_grouped_g32_one_expert_is_the_plain_gemm():
+    qa, sa, qb, sb = _g32_operands(40, 70, 256, seed=40)
+    ref, absum = oracle.m_grouped_gemm_nt_g32(qa, sa, qb[None], sb[None], np.zeros(40, np.int32))
+    want, wabs = oracle.gemm_nt_g32(qa, sa, qb, sb)
+    assert np.array_equal(ref, want) and np.array_equal(absum, wabs)
+
+
+def test_grouped_g32_matches_block_oracle_when_groups_share_a_scale():
+    # every expert's rows of B share one scale per 128x128 block and K block, and A's four
+    # 32-groups of a 128-block share one scale: the C implementation of the 128-block
+    # grouped oracle must then agree
+    m_idx = si.grouped_layout([50, 130, 7])
+    m, n, k, E = m_idx.size, 200, 512, 3
+    qa, sa, _, _ = _g32_operands(m, 8, k, seed=41)
+    sa128 = sa[:, ::4].copy()
+    rng = np.random.default_rng(42)
+    qb = rng.integers(0, 0x7F, (E, n, k)).astype(np.uint8) | (rng.integers(0, 2, (E, n, k)) << 7).astype(np.uint8)
+    sb_blk = np.ldexp(1.0, rng.integers(-3, 4, (E, -(-n // 128), k // 128))).astype(np.float32)
+    sb32 = np.repeat(np.repeat(sb_blk, 128, axis=1)[:, :n], 4, axis=2)
+    ref, _ = oracle.m_grouped_gemm_nt_g32(qa, np.repeat(sa128, 4, axis=1), qb, sb32, m_idx)
+    want, _ = oracle.m_grouped_gemm_nt(qa, sa128, qb, sb_blk, m_idx)
+    pad = m_idx < 0
+    assert np.isnan(ref[pad]).all() and np.isnan(want[pad]).all()
+    assert np.allclose(ref[~pad], want[~pad], rtol=1e-13, atol=0)
