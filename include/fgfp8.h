@@ -4,7 +4,8 @@
  *
  * Plain C: pointers, sizes and an opaque stream.  Every pointer named as a
  * tensor below is DEVICE memory owned by the caller; the library allocates
- * nothing and keeps no state beyond a per-device "is this gfx950" check.
+ * nothing and keeps no state beyond a per-device "is this gfx950" check and
+ * the runtime's occupancy figures for its persistent cast kernels.
  * `stream` is a hipStream_t passed as void* (NULL = the default stream).
  * Every call is asynchronous and stream-ordered; none synchronises the host.
  *
@@ -27,7 +28,7 @@
  *
  * Sources (web pages, cited by title and section):
  *   "DeepGEMM Essentials: High-Performance FP8 Matrix Multiplication"
- *     (dev.to), Parts 1, 3-6, 12-13, 18;
+ *     (dev.to), Parts 1, 3-6, 8-13, 18;
  *   "[Help] Starter script for nn.Linear for fwd,bwd" (DeepGEMM issue #102):
  *     forward / dgrad / wgrad composition and the RHS scale-row layout;
  *   "deep-gemm: fused per-token FP8 cast in Triton" (kernels-community PR
