@@ -91,6 +91,23 @@ class Linear:
             ("cast_dYT", lambda: fg.cast_per_token(self.dY.t(), self.dYTq, self.sdYT, 128, fg.SF_FP32)),
         ]
 
+    def ue8m0_ops(self):
+        """The same step with the casts' UE8M0 option (every scale a power of two, stored as
+        fp32): forward and dgrad still promote by the fp32-stored block scale of W, while the
+        weight gradient, whose two operands both carry 1x128 UE8M0 scales, runs on the scaled
+        MFMA without promotion.  Reuses the step's buffers."""
+        fg = self.fg
+        U = fg.SF_UE8M0
+        return [
+            ("cast_x_dual_ue8m0", lambda: fg.cast_per_token_dual(self.x, self.xq, self.sx, self.xTq, self.sxT, U)),
+            ("cast_W_ue8m0", lambda: fg.cast_per_block(self.W, self.Wq, self.sW, self.WqT, self.sWT, U)),
+            ("gemm_fwd_ue8m0", lambda: fg.gemm_fp8_nt_bf16(self.xq, self.sx, self.Wq, self.sW, self.y, U)),
+            ("cast_dY_dual_ue8m0", lambda: fg.cast_per_token_dual(self.dY, self.dYq, self.sdY, self.dYTq, self.sdYT, U)),
+            ("gemm_dgrad_ue8m0", lambda: fg.gemm_fp8_nt_bf16(self.dYq, self.sdY, self.WqT, self.sWT, self.dX, U)),
+            ("gemm_wgrad_ue8m0", lambda: fg.wgrad_gemm_fp8_nt_fp32_ue8m0(self.dYTq, self.sdYT, self.xTq, self.sxT,
+                                                                        self.dW, U)),
+        ]
+
     def g32_ops(self):
         """The same step in the UE8M0 group-32 recipe: x, W and dY each cast once in both
         orientations with 32-wide groups and packed UE8M0 scales (x, xT; W, WT; dY, dYT), and
@@ -123,6 +140,9 @@ class Linear:
             "cast_x": ("GB/s", tok(T, I)), "cast_xT": ("GB/s", tok(I, T)),
             "cast_dY": ("GB/s", tok(T, O)), "cast_dYT": ("GB/s", tok(O, T)),
             "gemm_fwd": ("TFLOPS", f), "gemm_dgrad": ("TFLOPS", f), "gemm_wgrad": ("TFLOPS", f),
+            "cast_x_dual_ue8m0": ("GB/s", dual(T, I)), "cast_W_ue8m0": ("GB/s", blk),
+            "cast_dY_dual_ue8m0": ("GB/s", dual(T, O)),
+            "gemm_fwd_ue8m0": ("TFLOPS", f), "gemm_dgrad_ue8m0": ("TFLOPS", f), "gemm_wgrad_ue8m0": ("TFLOPS", f),
             "cast_x_dual_g32": ("GB/s", dual(T, I)), "cast_W_dual_g32": ("GB/s", dual(O, I)),
             "cast_dY_dual_g32": ("GB/s", dual(T, O)),
             "gemm_fwd_g32": ("TFLOPS", f), "gemm_dgrad_g32": ("TFLOPS", f), "gemm_wgrad_g32": ("TFLOPS", f),
@@ -491,6 +511,12 @@ def main():
         result["extra"]["linear_step_separate_casts"] = {
             name: _measure(torch, *work[name], fn) for name, fn in lin.separate_cast_ops()}
         result["extra"]["forward_with_output_cast"] = fused_output_cast(fg, torch, lin)
+        ue = lin.ue8m0_ops()
+        u_ms, u_per = timed_ops(torch, ue, 10, 2)
+        u_ms /= 10
+        result["extra"]["linear_step_ue8m0_scales"] = {
+            "ms_per_step": u_ms, "tflops": flops_step / (u_ms * 1e-3) / 1e12,
+            "kernels": {name: rate(*work[name], u_per[name]) for name in u_per}}
         g32 = lin.g32_ops()
         g_ms, g_per = timed_ops(torch, g32, 10, 2)
         g_ms /= 10

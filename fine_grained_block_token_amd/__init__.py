@@ -48,6 +48,7 @@ def load():
                                           i64, i64, i64, p]
     lib.gemm_fp8_nt_bf16_ue8m0_g32.argtypes = [p, i64, p, i64, p, i64, p, i64, p, i64, i64, i64, i64, p]
     lib.wgrad_gemm_fp8_nt_fp32_ue8m0_g32.argtypes = [p, i64, p, i64, p, i64, p, i64, p, i64, i64, i64, i64, p]
+    lib.wgrad_gemm_fp8_nt_fp32_ue8m0.argtypes = [p, i64, p, i32, i64, p, i64, p, i64, p, i64, i64, i64, i64, p]
     lib.m_grouped_gemm_fp8_nt_bf16_ue8m0_g32_contiguous.argtypes = [p, i64, p, i64, p, i64, i64, p, i64, i64, p, i64,
                                                                     p, i64, i64, i64, i64, p]
     lib.m_grouped_gemm_fp8_nt_bf16_contiguous.argtypes = [p, i64, p, i32, i64, p, i64, i64, p, i64, i64, p, i64,
@@ -55,7 +56,7 @@ def load():
     for f in ("cast_per_token", "cast_per_block", "cast_per_token_dual", "gemm_fp8_nt_bf16",
               "wgrad_gemm_fp8_nt_fp32", "m_grouped_gemm_fp8_nt_bf16_contiguous", "gemm_fp8_nt_bf16_cast",
               "gemm_fp8_nt_bf16_ue8m0_g32", "wgrad_gemm_fp8_nt_fp32_ue8m0_g32",
-              "m_grouped_gemm_fp8_nt_bf16_ue8m0_g32_contiguous"):
+              "m_grouped_gemm_fp8_nt_bf16_ue8m0_g32_contiguous", "wgrad_gemm_fp8_nt_fp32_ue8m0"):
         getattr(lib, f).restype = i32
     lib.fgfp8_status_string.argtypes = [i32]
     lib.fgfp8_status_string.restype = ctypes.c_char_p
@@ -66,7 +67,8 @@ def load():
 EXPORTED = ("cast_per_token", "cast_per_block", "cast_per_token_dual", "gemm_fp8_nt_bf16",
             "wgrad_gemm_fp8_nt_fp32", "m_grouped_gemm_fp8_nt_bf16_contiguous", "gemm_fp8_nt_bf16_cast",
             "gemm_fp8_nt_bf16_ue8m0_g32", "wgrad_gemm_fp8_nt_fp32_ue8m0_g32",
-            "m_grouped_gemm_fp8_nt_bf16_ue8m0_g32_contiguous", "fgfp8_status_string")
+            "m_grouped_gemm_fp8_nt_bf16_ue8m0_g32_contiguous", "wgrad_gemm_fp8_nt_fp32_ue8m0",
+            "fgfp8_status_string")
 
 
 def _check(rc: int, what: str):
@@ -204,6 +206,24 @@ def gemm_fp8_nt_bf16_ue8m0_g32(A: torch.Tensor, sa: torch.Tensor, B: torch.Tenso
     _check(load().gemm_fp8_nt_bf16_ue8m0_g32(_ptr(A), A.stride(0), _ptr(sa), sa_ld, _ptr(B), B.stride(0), _ptr(sb),
                                              sb_ld, _ptr(D), D.stride(0), m, n, k, _stream(A)),
            "gemm_fp8_nt_bf16_ue8m0_g32")
+
+
+def wgrad_gemm_fp8_nt_fp32_ue8m0(A: torch.Tensor, sa: torch.Tensor, B: torch.Tensor, sb: torch.Tensor,
+                                 D: torch.Tensor, sf_fmt: int = SF_UE8M0) -> None:
+    """wgrad_gemm_fp8_nt_fp32 for power-of-two 1x128 scales on both operands, applied by the
+    scaled MFMA (no promotion): sa [m, k/128] / sb [n, k/128] float32 2^e values (SF_UE8M0) or
+    [m, ceil(k/512)] / [n, ceil(k/512)] int32 packed words (SF_PACKED_UE8M0), MN-major views."""
+    A, B = _u8(A), _u8(B)
+    m, k = A.shape
+    n = B.shape[0]
+    for s_ in (sa, sb):
+        if s_.shape[0] > 1 and s_.stride(0) != 1:
+            raise ValueError("scales must be MN-major (stride(0) == 1)")
+    sa_ld = sa.stride(1) if sa.dim() == 2 else m
+    sb_ld = sb.stride(1) if sb.dim() == 2 else n
+    _check(load().wgrad_gemm_fp8_nt_fp32_ue8m0(_ptr(A), A.stride(0), _ptr(sa), sf_fmt, sa_ld, _ptr(B), B.stride(0),
+                                               _ptr(sb), sb_ld, _ptr(D), D.stride(0), m, n, k, _stream(A)),
+           "wgrad_gemm_fp8_nt_fp32_ue8m0")
 
 
 def wgrad_gemm_fp8_nt_fp32_ue8m0_g32(A: torch.Tensor, sa: torch.Tensor, B: torch.Tensor, sb: torch.Tensor,

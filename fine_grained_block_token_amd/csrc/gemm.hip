@@ -440,7 +440,13 @@ __device__ __forceinline__ v8i frag_g32(const uint8_t *tile, int row, int lane) 
   return r;
 }
 
-template <class C, bool WGRAD, bool GROUPED>
+// Exponent layouts of the scaled-MFMA kernel: kUeG32Packed, one word per row and
+// 128-K block holding its four 32-K groups' bytes; kUeG128Packed, one word per row
+// and four 128-K blocks (byte kb%4 of word kb/4); kUeG128Float, one fp32 2^e per
+// row and 128-K block (the UE8M0 per-token cast), whose bits 30-23 are e+127.
+enum : int { kUeG32Packed = 0, kUeG128Packed = 1, kUeG128Float = 2 };
+
+template <class C, bool WGRAD, bool GROUPED, int SMODE = kUeG32Packed>
 __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_g32_kernel(GemmArgs g, int tiles_m, int tiles_n) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::kStages * C::kStageBytes];
   const int t = threadIdx.x, lane = t & 63;
@@ -501,22 +507,25 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_g32_kernel(Ge
     for (int i = 0; i < C::kALoads; ++i) load_lds16(ga, a_off[i], st + 1024 * (i * C::kWaves + wv));
 #pragma unroll
     for (int i = 0; i < C::kBLoads; ++i) load_lds16(gb, b_off[i], st + C::kABytes + 1024 * (i * C::kWaves + wv));
+    const int64_t col = SMODE == kUeG128Packed ? (kb >> 2) : kb;
     if (sa_loader) {
-      load_lds4(saw + (int64_t)kb * g.sa_ld + m0, scale_off, st + C::kSaOff + 256 * wv);
+      load_lds4(saw + col * g.sa_ld + m0, scale_off, st + C::kSaOff + 256 * wv);
     } else if (sb_loader) {
-      load_lds4(sbw + (int64_t)kb * g.sb_ld + n0, scale_off, st + C::kSbOff + 256 * (wv - C::kSaLoads));
+      load_lds4(sbw + col * g.sb_ld + n0, scale_off, st + C::kSbOff + 256 * (wv - C::kSaLoads));
     }
   };
 
   v4f acc[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc[i] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
-  const int gsh = 8 * (lane >> 4);   // this lane's 32-K group within the block
+  // this lane's 32-K group within the block (group 32), or the block's byte of its word
+  const int gsh0 = SMODE == kUeG32Packed ? 8 * (lane >> 4) : SMODE == kUeG128Float ? 23 : 0;
   issue(0, smem);
   for (int kb = 0; kb < KB; ++kb) {
     asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier\n\ts_setprio 0" ::: "memory");
     const uint8_t *st = smem + (kb & 1) * C::kStageBytes;
     if (kb + 1 < KB) issue(kb + 1, smem + ((kb + 1) & 1) * C::kStageBytes);
+    const int gsh = SMODE == kUeG128Packed ? 8 * (kb & 3) : gsh0;
     int ea[4], eb[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -746,7 +755,14 @@ hipError_t launch_gemm_g32(const GemmArgs &a, hipStream_t st) {
   const int tiles_m = (int)((a.m + C::kBM - 1) / C::kBM), tiles_n = (int)((a.n + C::kBN - 1) / C::kBN);
   const int per_xcd = (tiles_m * tiles_n + kXcds - 1) / kXcds;
   const dim3 grid((unsigned)(per_xcd * kXcds));
-  if (a.wgrad)
+  if (a.wgrad && a.ue_gran == 128)   // UE8M0 1x128 scales on both operands
+    if (a.sa_fmt == kSfPackedUe8m0)
+      hipLaunchKernelGGL((gemm_g32_kernel<C, true, false, kUeG128Packed>), grid, dim3(C::kThreads), 0, st, a, tiles_m,
+                         tiles_n);
+    else
+      hipLaunchKernelGGL((gemm_g32_kernel<C, true, false, kUeG128Float>), grid, dim3(C::kThreads), 0, st, a, tiles_m,
+                         tiles_n);
+  else if (a.wgrad)
     hipLaunchKernelGGL((gemm_g32_kernel<C, true, false>), grid, dim3(C::kThreads), 0, st, a, tiles_m, tiles_n);
   else if (a.m_idx != nullptr)
     hipLaunchKernelGGL((gemm_g32_kernel<C, false, true>), grid, dim3(C::kThreads), 0, st, a, tiles_m, tiles_n);

@@ -82,6 +82,10 @@ struct GemmArgs {
   float *cq_sf = nullptr;
   int64_t cq_s_row = 0, cq_s_grp = 0;
   int cq_fmt = 0;
+  // Scaled-MFMA kernel (launch_gemm_g32): group size of the UE8M0 exponents, 32
+  // (packed words) or 128 (wgrad only: packed words, or fp32 2^e values when
+  // sa_fmt is kSfUe8m0).
+  int ue_gran = 32;
 };
 
 hipError_t launch_cast_per_token(const CastTokenArgs &a, hipStream_t st);

@@ -231,6 +231,28 @@ int gemm_fp8_nt_bf16_ue8m0_g32(const uint8_t *A, int64_t lda, const uint32_t *sa
                                void *stream);
 
 /*
+ * wgrad_gemm_fp8_nt_fp32_ue8m0 -- wgrad_gemm_fp8_nt_fp32 for operands whose
+ * 1x128 per-token scales are powers of two on both sides (the UE8M0 option of
+ * the per-token cast: "deep-gemm: fused per-token FP8 cast in Triton"; the
+ * weight gradient of "DeepGEMM Essentials", Parts 12-13):
+ *     D[i, j] += sum_kb 2^(ea(i,kb) + eb(j,kb)) sum_{t in kb} A[i, t] B[j, t].
+ * The result equals wgrad_gemm_fp8_nt_fp32 on the same scales as fp32 values
+ * up to rounding order: the exponents are applied by the scaled FP8 MFMA,
+ * which accumulates across K in fp32, so no per-block promotion is needed.
+ *
+ * sf_fmt   FGFP8_SF_UE8M0: sa, sb are fp32 2^e values, (i, kb) at
+ *          sa[kb*sa_ld + i] and (j, kb) at sb[kb*sb_ld + j] (what
+ *          cast_per_token writes with gran_k = 128 into MN-major views);
+ *          FGFP8_SF_PACKED_UE8M0: int32 words, byte kb%4 of word
+ *          (i, kb/4) at sa[(kb/4)*sa_ld + i] is ea(i, kb) + 127 (likewise sb).
+ * A, lda, sa_ld, B, ldb, sb_ld, D, ldd, m, n, k   as wgrad_gemm_fp8_nt_fp32
+ *          (sa_ld >= m, sb_ld >= n).
+ */
+int wgrad_gemm_fp8_nt_fp32_ue8m0(const uint8_t *A, int64_t lda, const void *sa, int sf_fmt, int64_t sa_ld,
+                                 const uint8_t *B, int64_t ldb, const void *sb, int64_t sb_ld,
+                                 float *D, int64_t ldd, int64_t m, int64_t n, int64_t k, void *stream);
+
+/*
  * wgrad_gemm_fp8_nt_fp32_ue8m0_g32 -- the weight-gradient form of the UE8M0
  * group-32 recipe: D += (A * sa)(B * sb)^T in fp32, with K running over tokens
  * ("DeepGEMM Essentials", Parts 12-13: dW = dY^T x, fp32 output accumulated in

@@ -281,3 +281,76 @@ def test_wgrad_linear_size_sampled(gpu):
     ref, absum = oracle.wgrad_nt(qa, sa, qb, sb, zero, idx=(ii, jj))
     tb = mfma_truncation_bound(qa, sa, qb, sb, sb_block=False, idx=(ii, jj))
     _check_wgrad(got[ii, jj], ref, absum, tb, tokens // 128, "wgrad 4096x7168x8192")
+
+
+# wgrad with UE8M0 1x128 scales on both operands (the cast's UE8M0 option): the exponents
+# are applied by the scaled MFMA, which accumulates all of K in fp32, so the fp32
+# accumulation term counts one rounding per run of 8 tokens: (K/8 + 20) 2^-24 (...).
+
+def _wgrad_operands_ue8m0(tokens, d_out, d_in, fmt):
+    dy = si.randn((tokens, d_out), si.SEED_DY)
+    x = si.randn((tokens, d_in), si.SEED_A)
+    qa, sa = oracle.cast_per_token(si.host_array(dy), 128, fmt, transpose=True)
+    qb, sb = oracle.cast_per_token(si.host_array(x), 128, fmt, transpose=True)
+    return qa, sa, qb, sb
+
+
+def _run_wgrad_ue8m0(qa, sa, qb, sb, d_in_np, fmt, times=1):
+    m, k = qa.shape
+    n = qb.shape[0]
+    ldd = -(-n // 4) * 4 + 4
+    D = torch.full((m, ldd), -1.0, dtype=torch.float32)
+    D[:, :n] = torch.from_numpy(d_in_np)
+    Dd = D.cuda()
+    dt = torch.int32 if fmt == fg.SF_PACKED_UE8M0 else torch.float32
+    A, B, sa_d, sb_d = torch.from_numpy(qa).cuda(), torch.from_numpy(qb).cuda(), _to_dev_mn(sa, dt), _to_dev_mn(sb, dt)
+    for _ in range(times):
+        say("wgrad_gemm_fp8_nt_fp32_ue8m0", (m, n, k), "fmt", fmt)
+        fg.wgrad_gemm_fp8_nt_fp32_ue8m0(A, sa_d, B, sb_d, Dd[:, :n], fmt)
+    torch.cuda.synchronize()
+    out = Dd.cpu().numpy()
+    assert (out[:, n:] == -1.0).all()
+    return out[:, :n]
+
+
+@pytest.mark.parametrize("shape", [(256, 512, 1024), (384, 130, 200), (1024, 256, 128), (640, 250, 38360)])
+@pytest.mark.parametrize("fmt", [fg.SF_UE8M0, fg.SF_PACKED_UE8M0], ids=["ue8m0", "packed"])
+def test_wgrad_ue8m0_full_compare(gpu, shape, fmt):
+    tokens, d_out, d_in = shape
+    qa, sa, qb, sb = _wgrad_operands_ue8m0(tokens, d_out, d_in, fmt)
+    if fmt == fg.SF_PACKED_UE8M0:
+        sa_v, sb_v = oracle.unpack_ue8m0(sa, tokens // 128), oracle.unpack_ue8m0(sb, tokens // 128)
+    else:
+        sa_v, sb_v = sa, sb
+    d_in_np = si.randn((d_out, d_in), 8, 0.1, torch.float32).numpy()
+    got = _run_wgrad_ue8m0(qa, sa, qb, sb, d_in_np, fmt)
+    ref, absum = oracle.wgrad_nt(qa, sa_v, qb, sb_v, d_in_np)
+    tb = mfma_truncation_bound(qa, sa_v, qb, sb_v, sb_block=False)
+    _check_wgrad(got, ref, absum, tb, tokens // 8, f"wgrad ue8m0 {shape} fmt {fmt}")
+
+
+def test_wgrad_ue8m0_closed_form_accumulates(gpu):
+    # all-ones operands with a power of two per (row, K block): exact, so two calls give
+    # D_in + 2 * sum_kb 128 * 2^(ea + eb)
+    m, n, k = 130, 260, 640
+    rng = np.random.default_rng(24)
+    ea = rng.integers(-5, 6, (m, k // 128))
+    eb = rng.integers(-5, 6, (n, k // 128))
+    sa, sb = np.ldexp(1.0, ea).astype(np.float32), np.ldexp(1.0, eb).astype(np.float32)
+    d_in = rng.integers(-64, 65, (m, n)).astype(np.float32)
+    got = _run_wgrad_ue8m0(np.full((m, k), 0x38, np.uint8), sa, np.full((n, k), 0x38, np.uint8), sb, d_in,
+                           fg.SF_UE8M0, times=2)
+    want = d_in.astype(np.float64) + 2 * 128 * (np.ldexp(1.0, ea)[:, None, :] * np.ldexp(1.0, eb)[None, :, :]).sum(axis=2)
+    assert np.array_equal(got.astype(np.float64), want)
+
+
+def test_wgrad_ue8m0_linear_size_sampled(gpu):
+    tokens, d_out, d_in = si.LINEAR["tokens"], si.LINEAR["d_out"], si.LINEAR["d_in"]
+    qa, sa, qb, sb = _wgrad_operands_ue8m0(tokens, d_out, d_in, fg.SF_PACKED_UE8M0)
+    sa_v, sb_v = oracle.unpack_ue8m0(sa, tokens // 128), oracle.unpack_ue8m0(sb, tokens // 128)
+    zero = np.zeros((d_out, d_in), np.float32)
+    got = _run_wgrad_ue8m0(qa, sa, qb, sb, zero, fg.SF_PACKED_UE8M0)
+    ii, jj = _sample_idx(d_out, d_in, 20000, 11)
+    ref, absum = oracle.wgrad_nt(qa, sa_v, qb, sb_v, zero, idx=(ii, jj))
+    tb = mfma_truncation_bound(qa, sa_v, qb, sb_v, sb_block=False, idx=(ii, jj))
+    _check_wgrad(got[ii, jj], ref, absum, tb, tokens // 8, "wgrad ue8m0 4096x7168x8192")
