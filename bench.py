@@ -93,17 +93,17 @@ class Linear:
 
     def ue8m0_ops(self):
         """The same step with the casts' UE8M0 option (every scale a power of two, stored as
-        fp32): forward and dgrad still promote by the fp32-stored block scale of W, while the
-        weight gradient, whose two operands both carry 1x128 UE8M0 scales, runs on the scaled
-        MFMA without promotion.  Reuses the step's buffers."""
+        fp32): all three GEMMs apply the exponents on the scaled MFMA, without promotion.
+        Reuses the step's buffers."""
         fg = self.fg
         U = fg.SF_UE8M0
         return [
             ("cast_x_dual_ue8m0", lambda: fg.cast_per_token_dual(self.x, self.xq, self.sx, self.xTq, self.sxT, U)),
             ("cast_W_ue8m0", lambda: fg.cast_per_block(self.W, self.Wq, self.sW, self.WqT, self.sWT, U)),
-            ("gemm_fwd_ue8m0", lambda: fg.gemm_fp8_nt_bf16(self.xq, self.sx, self.Wq, self.sW, self.y, U)),
+            ("gemm_fwd_ue8m0", lambda: fg.gemm_fp8_nt_bf16_ue8m0(self.xq, self.sx, self.Wq, self.sW, self.y, U)),
             ("cast_dY_dual_ue8m0", lambda: fg.cast_per_token_dual(self.dY, self.dYq, self.sdY, self.dYTq, self.sdYT, U)),
-            ("gemm_dgrad_ue8m0", lambda: fg.gemm_fp8_nt_bf16(self.dYq, self.sdY, self.WqT, self.sWT, self.dX, U)),
+            ("gemm_dgrad_ue8m0", lambda: fg.gemm_fp8_nt_bf16_ue8m0(self.dYq, self.sdY, self.WqT, self.sWT, self.dX,
+                                                                  U)),
             ("gemm_wgrad_ue8m0", lambda: fg.wgrad_gemm_fp8_nt_fp32_ue8m0(self.dYTq, self.sdYT, self.xTq, self.sxT,
                                                                         self.dW, U)),
         ]

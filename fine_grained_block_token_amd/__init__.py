@@ -49,6 +49,7 @@ def load():
     lib.gemm_fp8_nt_bf16_ue8m0_g32.argtypes = [p, i64, p, i64, p, i64, p, i64, p, i64, i64, i64, i64, p]
     lib.wgrad_gemm_fp8_nt_fp32_ue8m0_g32.argtypes = [p, i64, p, i64, p, i64, p, i64, p, i64, i64, i64, i64, p]
     lib.wgrad_gemm_fp8_nt_fp32_ue8m0.argtypes = [p, i64, p, i32, i64, p, i64, p, i64, p, i64, i64, i64, i64, p]
+    lib.gemm_fp8_nt_bf16_ue8m0.argtypes = [p, i64, p, i32, i64, p, i64, p, i64, p, i64, i64, i64, i64, p]
     lib.m_grouped_gemm_fp8_nt_bf16_ue8m0_g32_contiguous.argtypes = [p, i64, p, i64, p, i64, i64, p, i64, i64, p, i64,
                                                                     p, i64, i64, i64, i64, p]
     lib.m_grouped_gemm_fp8_nt_bf16_contiguous.argtypes = [p, i64, p, i32, i64, p, i64, i64, p, i64, i64, p, i64,
@@ -56,7 +57,8 @@ def load():
     for f in ("cast_per_token", "cast_per_block", "cast_per_token_dual", "gemm_fp8_nt_bf16",
               "wgrad_gemm_fp8_nt_fp32", "m_grouped_gemm_fp8_nt_bf16_contiguous", "gemm_fp8_nt_bf16_cast",
               "gemm_fp8_nt_bf16_ue8m0_g32", "wgrad_gemm_fp8_nt_fp32_ue8m0_g32",
-              "m_grouped_gemm_fp8_nt_bf16_ue8m0_g32_contiguous", "wgrad_gemm_fp8_nt_fp32_ue8m0"):
+              "m_grouped_gemm_fp8_nt_bf16_ue8m0_g32_contiguous", "wgrad_gemm_fp8_nt_fp32_ue8m0",
+              "gemm_fp8_nt_bf16_ue8m0"):
         getattr(lib, f).restype = i32
     lib.fgfp8_status_string.argtypes = [i32]
     lib.fgfp8_status_string.restype = ctypes.c_char_p
@@ -68,7 +70,7 @@ EXPORTED = ("cast_per_token", "cast_per_block", "cast_per_token_dual", "gemm_fp8
             "wgrad_gemm_fp8_nt_fp32", "m_grouped_gemm_fp8_nt_bf16_contiguous", "gemm_fp8_nt_bf16_cast",
             "gemm_fp8_nt_bf16_ue8m0_g32", "wgrad_gemm_fp8_nt_fp32_ue8m0_g32",
             "m_grouped_gemm_fp8_nt_bf16_ue8m0_g32_contiguous", "wgrad_gemm_fp8_nt_fp32_ue8m0",
-            "fgfp8_status_string")
+            "gemm_fp8_nt_bf16_ue8m0", "fgfp8_status_string")
 
 
 def _check(rc: int, what: str):
@@ -206,6 +208,22 @@ def gemm_fp8_nt_bf16_ue8m0_g32(A: torch.Tensor, sa: torch.Tensor, B: torch.Tenso
     _check(load().gemm_fp8_nt_bf16_ue8m0_g32(_ptr(A), A.stride(0), _ptr(sa), sa_ld, _ptr(B), B.stride(0), _ptr(sb),
                                              sb_ld, _ptr(D), D.stride(0), m, n, k, _stream(A)),
            "gemm_fp8_nt_bf16_ue8m0_g32")
+
+
+def gemm_fp8_nt_bf16_ue8m0(A: torch.Tensor, sa: torch.Tensor, B: torch.Tensor, sb: torch.Tensor, D: torch.Tensor,
+                           sa_fmt: int = SF_UE8M0) -> None:
+    """gemm_fp8_nt_bf16 with power-of-two scales throughout, applied by the scaled MFMA (no
+    promotion): sa [m, k/128] float32 2^e (SF_UE8M0) or [m, ceil(k/512)] int32 packed words,
+    MN-major; sb [ceil(n/128), k/128] float32 2^e block scales."""
+    A, B = _u8(A), _u8(B)
+    m, k = A.shape
+    n = B.shape[0]
+    if sa.shape[0] > 1 and sa.stride(0) != 1:
+        raise ValueError("sa must be MN-major (stride(0) == 1)")
+    sa_ld = sa.stride(1) if sa.dim() == 2 else m
+    _check(load().gemm_fp8_nt_bf16_ue8m0(_ptr(A), A.stride(0), _ptr(sa), sa_fmt, sa_ld, _ptr(B), B.stride(0), _ptr(sb),
+                                         sb.stride(0), _ptr(D), D.stride(0), m, n, k, _stream(A)),
+           "gemm_fp8_nt_bf16_ue8m0")
 
 
 def wgrad_gemm_fp8_nt_fp32_ue8m0(A: torch.Tensor, sa: torch.Tensor, B: torch.Tensor, sb: torch.Tensor,

@@ -202,6 +202,21 @@ int gemm_fp8_nt_bf16_ue8m0_g32(const uint8_t *A, int64_t lda, const uint32_t *sa
   return launched(fgfp8::launch_gemm_g32(a, static_cast<hipStream_t>(stream)));
 }
 
+int gemm_fp8_nt_bf16_ue8m0(const uint8_t *A, int64_t lda, const void *sa, int sa_fmt, int64_t sa_ld,
+                           const uint8_t *B, int64_t ldb, const float *sb, int64_t sb_ld, uint16_t *D, int64_t ldd,
+                           int64_t m, int64_t n, int64_t k, void *stream) {
+  if (sa_fmt != kSfUe8m0 && sa_fmt != kSfPackedUe8m0) return FGFP8_EINVAL;
+  const int c = check_gemm_common(A, lda, sa, sa_ld, B, ldb, sb, D, m, n, k);
+  if (c != 1) return c;
+  if (sb_ld < k / 128) return FGFP8_EINVAL;
+  if (!aligned(D, 16) || ldd < n || ldd % 8 != 0) return FGFP8_EINVAL;
+  const int dev = check_device();
+  if (dev != FGFP8_OK) return dev;
+  fgfp8::GemmArgs a{A, lda, sa, sa_fmt, sa_ld, B, ldb, sb, sb_ld, D, ldd, m, n, k, false};
+  a.ue_gran = 128;
+  return launched(fgfp8::launch_gemm_g32(a, static_cast<hipStream_t>(stream)));
+}
+
 int wgrad_gemm_fp8_nt_fp32_ue8m0(const uint8_t *A, int64_t lda, const void *sa, int sf_fmt, int64_t sa_ld,
                                  const uint8_t *B, int64_t ldb, const void *sb, int64_t sb_ld, float *D, int64_t ldd,
                                  int64_t m, int64_t n, int64_t k, void *stream) {

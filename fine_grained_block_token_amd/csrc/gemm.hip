@@ -444,9 +444,11 @@ __device__ __forceinline__ v8i frag_g32(const uint8_t *tile, int row, int lane) 
 // 128-K block holding its four 32-K groups' bytes; kUeG128Packed, one word per row
 // and four 128-K blocks (byte kb%4 of word kb/4); kUeG128Float, one fp32 2^e per
 // row and 128-K block (the UE8M0 per-token cast), whose bits 30-23 are e+127.
-enum : int { kUeG32Packed = 0, kUeG128Packed = 1, kUeG128Float = 2 };
+// kUeBlockFloat (B only): one fp32 2^e per 128x128 block of B, (nb, kb) at
+// sb[nb*sb_ld + kb], the same exponent for every column of the tile.
+enum : int { kUeG32Packed = 0, kUeG128Packed = 1, kUeG128Float = 2, kUeBlockFloat = 3 };
 
-template <class C, bool WGRAD, bool GROUPED, int SMODE = kUeG32Packed>
+template <class C, bool WGRAD, bool GROUPED, int SMODE = kUeG32Packed, int SB_MODE = SMODE>
 __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_g32_kernel(GemmArgs g, int tiles_m, int tiles_n) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::kStages * C::kStageBytes];
   const int t = threadIdx.x, lane = t & 63;
@@ -507,30 +509,40 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_g32_kernel(Ge
     for (int i = 0; i < C::kALoads; ++i) load_lds16(ga, a_off[i], st + 1024 * (i * C::kWaves + wv));
 #pragma unroll
     for (int i = 0; i < C::kBLoads; ++i) load_lds16(gb, b_off[i], st + C::kABytes + 1024 * (i * C::kWaves + wv));
-    const int64_t col = SMODE == kUeG128Packed ? (kb >> 2) : kb;
     if (sa_loader) {
+      const int64_t col = SMODE == kUeG128Packed ? (kb >> 2) : kb;
       load_lds4(saw + col * g.sa_ld + m0, scale_off, st + C::kSaOff + 256 * wv);
     } else if (sb_loader) {
-      load_lds4(sbw + col * g.sb_ld + n0, scale_off, st + C::kSbOff + 256 * (wv - C::kSaLoads));
+      if constexpr (SB_MODE == kUeBlockFloat) {   // the tile's one block scale, the same dword in every lane
+        load_lds4(sbw + (n0 >> 7) * g.sb_ld + kb, 0u, st + C::kSbOff + 256 * (wv - C::kSaLoads));
+      } else {
+        const int64_t col = SB_MODE == kUeG128Packed ? (kb >> 2) : kb;
+        load_lds4(sbw + col * g.sb_ld + n0, scale_off, st + C::kSbOff + 256 * (wv - C::kSaLoads));
+      }
     }
   };
 
   v4f acc[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc[i] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
-  // this lane's 32-K group within the block (group 32), or the block's byte of its word
-  const int gsh0 = SMODE == kUeG32Packed ? 8 * (lane >> 4) : SMODE == kUeG128Float ? 23 : 0;
+  // this lane's 32-K group within the block (group 32), the fp32 exponent field, or
+  // (packed group 128, below) the block's byte of its word
+  auto shift0 = [&](int mode) { return mode == kUeG32Packed ? 8 * (lane >> 4) : mode == kUeG128Packed ? 0 : 23; };
+  const int gsh_a0 = shift0(SMODE), gsh_b0 = shift0(SB_MODE);
   issue(0, smem);
   for (int kb = 0; kb < KB; ++kb) {
     asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier\n\ts_setprio 0" ::: "memory");
     const uint8_t *st = smem + (kb & 1) * C::kStageBytes;
     if (kb + 1 < KB) issue(kb + 1, smem + ((kb + 1) & 1) * C::kStageBytes);
-    const int gsh = SMODE == kUeG128Packed ? 8 * (kb & 3) : gsh0;
+    const int gsh_a = SMODE == kUeG128Packed ? 8 * (kb & 3) : gsh_a0;
+    const int gsh_b = SB_MODE == kUeG128Packed ? 8 * (kb & 3) : gsh_b0;
     int ea[4], eb[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      ea[i] = (int)((*reinterpret_cast<const uint32_t *>(st + C::kSaOff + 4 * (wm + 16 * i + (lane & 15))) >> gsh) & 0xFFu);
-      eb[i] = (int)((*reinterpret_cast<const uint32_t *>(st + C::kSbOff + 4 * (wn + 16 * i + (lane & 15))) >> gsh) & 0xFFu);
+      ea[i] = (int)((*reinterpret_cast<const uint32_t *>(st + C::kSaOff + 4 * (wm + 16 * i + (lane & 15))) >> gsh_a) &
+                    0xFFu);
+      const int bo = SB_MODE == kUeBlockFloat ? 0 : 4 * (wn + 16 * i + (lane & 15));
+      eb[i] = (int)((*reinterpret_cast<const uint32_t *>(st + C::kSbOff + bo) >> gsh_b) & 0xFFu);
     }
     v8i af[4], bf[4];
     af[0] = frag_g32(st, wm + (lane & 15), lane);
@@ -764,6 +776,13 @@ hipError_t launch_gemm_g32(const GemmArgs &a, hipStream_t st) {
                          tiles_n);
   else if (a.wgrad)
     hipLaunchKernelGGL((gemm_g32_kernel<C, true, false>), grid, dim3(C::kThreads), 0, st, a, tiles_m, tiles_n);
+  else if (a.ue_gran == 128)   // forward / dgrad with UE8M0 1x128 A scales and 128x128 B block scales
+    if (a.sa_fmt == kSfPackedUe8m0)
+      hipLaunchKernelGGL((gemm_g32_kernel<C, false, false, kUeG128Packed, kUeBlockFloat>), grid, dim3(C::kThreads), 0,
+                         st, a, tiles_m, tiles_n);
+    else
+      hipLaunchKernelGGL((gemm_g32_kernel<C, false, false, kUeG128Float, kUeBlockFloat>), grid, dim3(C::kThreads), 0,
+                         st, a, tiles_m, tiles_n);
   else if (a.m_idx != nullptr)
     hipLaunchKernelGGL((gemm_g32_kernel<C, false, true>), grid, dim3(C::kThreads), 0, st, a, tiles_m, tiles_n);
   else

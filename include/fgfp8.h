@@ -231,6 +231,26 @@ int gemm_fp8_nt_bf16_ue8m0_g32(const uint8_t *A, int64_t lda, const uint32_t *sa
                                void *stream);
 
 /*
+ * gemm_fp8_nt_bf16_ue8m0 -- gemm_fp8_nt_bf16 when every scale is a power of
+ * two: A's 1x128 per-token scales and B's 128x128 block scales both come from
+ * the casts' UE8M0 option ("deep-gemm: fused per-token FP8 cast in Triton";
+ * the GEMM of "DeepGEMM Essentials", Parts 1 and 6):
+ *     D[i, j] = sum_kb 2^(ea(i,kb) + eb(j/128,kb)) sum_{t in kb} A[i, t] B[j, t],
+ * rounded to bf16.  The exponents are applied by the scaled FP8 MFMA, which
+ * accumulates across K in fp32: no per-block promotion.
+ *
+ * sa_fmt   FGFP8_SF_UE8M0 (sa fp32 2^e, (i, kb) at sa[kb*sa_ld + i]) or
+ *          FGFP8_SF_PACKED_UE8M0 (int32 words, byte kb%4 of word (i, kb/4) at
+ *          sa[(kb/4)*sa_ld + i] is ea(i, kb) + 127).
+ * sb       fp32 2^e [ceil(n/128), k/128], (nb, kb) at sb[nb*sb_ld + kb], as
+ *          cast_per_block writes with FGFP8_SF_UE8M0.
+ * A, lda, sa_ld, B, ldb, sb_ld, D, ldd, m, n, k   as gemm_fp8_nt_bf16.
+ */
+int gemm_fp8_nt_bf16_ue8m0(const uint8_t *A, int64_t lda, const void *sa, int sa_fmt, int64_t sa_ld,
+                           const uint8_t *B, int64_t ldb, const float *sb, int64_t sb_ld,
+                           uint16_t *D, int64_t ldd, int64_t m, int64_t n, int64_t k, void *stream);
+
+/*
  * wgrad_gemm_fp8_nt_fp32_ue8m0 -- wgrad_gemm_fp8_nt_fp32 for operands whose
  * 1x128 per-token scales are powers of two on both sides (the UE8M0 option of
  * the per-token cast: "deep-gemm: fused per-token FP8 cast in Triton"; the

@@ -29,7 +29,7 @@ def test_header_declares_the_entry_points():
               "wgrad_gemm_fp8_nt_fp32", "m_grouped_gemm_fp8_nt_bf16_contiguous", "gemm_fp8_nt_bf16_cast",
               "gemm_fp8_nt_bf16_ue8m0_g32", "wgrad_gemm_fp8_nt_fp32_ue8m0_g32",
               "m_grouped_gemm_fp8_nt_bf16_ue8m0_g32_contiguous", "wgrad_gemm_fp8_nt_fp32_ue8m0",
-              "fgfp8_status_string"):
+              "gemm_fp8_nt_bf16_ue8m0", "fgfp8_status_string"):
         assert f in names
 
 
@@ -265,3 +265,21 @@ def test_wgrad_ue8m0_rejects(lib, kw):
 
 def test_wgrad_ue8m0_zero_size_is_ok(lib):
     assert wue(lib, m=0) == 0 and wue(lib, n=0, fmt=2) == 0
+
+
+def gue(lib, **kw):
+    a = dict(A=P, lda=256, sa=S, fmt=1, sald=128, B=Q, ldb=256, sb=S, sbld=2, D=P, ldd=256, m=128, n=256, k=256,
+             st=None)
+    a.update(kw)
+    return lib.gemm_fp8_nt_bf16_ue8m0(a["A"], a["lda"], a["sa"], a["fmt"], a["sald"], a["B"], a["ldb"], a["sb"],
+                                      a["sbld"], a["D"], a["ldd"], a["m"], a["n"], a["k"], a["st"])
+
+
+@pytest.mark.parametrize("kw", [dict(fmt=0), dict(fmt=3), dict(sbld=1), dict(sald=127), dict(k=96), dict(sa=None),
+                                dict(sb=None), dict(D=None), dict(ldd=252), dict(D=ctypes.c_void_p(0x10008))])
+def test_gemm_ue8m0_rejects(lib, kw):
+    assert gue(lib, **kw) == -1
+
+
+def test_gemm_ue8m0_zero_size_is_ok(lib):
+    assert gue(lib, m=0) == 0 and gue(lib, n=0, fmt=2) == 0

@@ -354,3 +354,67 @@ def test_wgrad_ue8m0_linear_size_sampled(gpu):
     ref, absum = oracle.wgrad_nt(qa, sa_v, qb, sb_v, zero, idx=(ii, jj))
     tb = mfma_truncation_bound(qa, sa_v, qb, sb_v, sb_block=False, idx=(ii, jj))
     _check_wgrad(got[ii, jj], ref, absum, tb, tokens // 8, "wgrad ue8m0 4096x7168x8192")
+
+
+# forward GEMM with every scale a power of two (UE8M0 per-token A scales, UE8M0 128x128 B
+# block scales), applied by the scaled MFMA: tolerance as the plain GEMM with one fp32
+# rounding per run of 8 K products (K/8 + 20 in the accumulation term).
+
+def _cast_operands_ue8m0(m, n, k, a_fmt, scale=1.0):
+    a = si.randn((m, k), si.SEED_A, scale)
+    b = si.randn((n, k), si.SEED_B, scale)
+    qa, sa = oracle.cast_per_token(si.host_array(a), 128, a_fmt)
+    qb, sb = oracle.cast_per_block(si.host_array(b), oracle.SF_UE8M0)
+    return qa, sa, qb, sb
+
+
+def _run_gemm_ue8m0(qa, sa, qb, sb, sa_fmt):
+    m, k = qa.shape
+    n = qb.shape[0]
+    sa_d = _to_dev_mn(sa, torch.int32 if sa_fmt == fg.SF_PACKED_UE8M0 else torch.float32)
+    ldd = -(-n // 8) * 8
+    D = torch.full((m, ldd), 0x7FC0, dtype=torch.int16, device="cuda")
+    say("gemm_fp8_nt_bf16_ue8m0", (m, n, k), "sa_fmt", sa_fmt)
+    fg.gemm_fp8_nt_bf16_ue8m0(torch.from_numpy(qa).cuda(), sa_d, torch.from_numpy(qb).cuda(),
+                              torch.from_numpy(sb).cuda(), D[:, :n].view(torch.bfloat16), sa_fmt)
+    torch.cuda.synchronize()
+    Dh = D.cpu().numpy().view(np.uint16)
+    assert (Dh[:, n:] == 0x7FC0).all()
+    return Dh[:, :n]
+
+
+@pytest.mark.parametrize("mnk", [(128, 256, 512), (1, 128, 128), (129, 200, 256), (3, 300, 384), (257, 130, 640),
+                                 (256, 384, 7168), (250, 38360, 384)])
+@pytest.mark.parametrize("fmt", [fg.SF_UE8M0, fg.SF_PACKED_UE8M0], ids=["ue8m0", "packed"])
+def test_gemm_ue8m0_full_compare(gpu, mnk, fmt):
+    m, n, k = mnk
+    qa, sa, qb, sb = _cast_operands_ue8m0(m, n, k, fmt)
+    sa_v = oracle.unpack_ue8m0(sa, k // 128) if fmt == fg.SF_PACKED_UE8M0 else sa
+    got = _run_gemm_ue8m0(qa, sa, qb, sb, fmt)
+    ref, absum = oracle.gemm_nt(qa, sa_v, qb, sb)
+    check_bf16_gemm(got, ref, absum, mfma_truncation_bound(qa, sa_v, qb, sb), k // 8, f"gemm ue8m0 {mnk}")
+
+
+def test_gemm_ue8m0_closed_form_pins_scale_indexing(gpu):
+    # all-ones operands; per-(row, K block) and per-(128-column block, K block) exponents
+    m, n, k = 130, 300, 640
+    rng = np.random.default_rng(25)
+    ea = rng.integers(-5, 6, (m, k // 128))
+    eb = rng.integers(-5, 6, (-(-n // 128), k // 128))
+    sa, sb = np.ldexp(1.0, ea).astype(np.float32), np.ldexp(1.0, eb).astype(np.float32)
+    got = oracle.bf16_bits_to_f32(_run_gemm_ue8m0(np.full((m, k), 0x38, np.uint8), sa, np.full((n, k), 0x38, np.uint8),
+                                                  sb, fg.SF_UE8M0)).astype(np.float64)
+    ebj = np.repeat(eb, 128, axis=0)[:n]
+    want = 128 * (np.ldexp(1.0, ea)[:, None, :] * np.ldexp(1.0, ebj)[None, :, :]).sum(axis=2)
+    assert np.array_equal(got, oracle.bf16_bits_to_f32(oracle.round_bf16(want)).astype(np.float64))
+
+
+def test_gemm_ue8m0_prefill_sampled(gpu):
+    m, n, k = 4096, 7168, 7168
+    qa, sa, qb, sb = _cast_operands_ue8m0(m, n, k, fg.SF_PACKED_UE8M0, scale=0.1)
+    sa_v = oracle.unpack_ue8m0(sa, k // 128)
+    got = _run_gemm_ue8m0(qa, sa, qb, sb, fg.SF_PACKED_UE8M0)
+    ii, jj = _sample_idx(m, n, 20000, 12)
+    ref, absum = oracle.gemm_nt(qa, sa_v, qb, sb, idx=(ii, jj))
+    tb = mfma_truncation_bound(qa, sa_v, qb, sb, idx=(ii, jj))
+    check_bf16_gemm(got[ii, jj], ref, absum, tb, k // 8, "gemm ue8m0 prefill")

@@ -50,6 +50,11 @@ def test_graph_replays_match_eager(gpu):
     Wg32 = torch.empty((E, O, I), dtype=u8, device="cuda")
     sWg32 = torch.empty((E, I // 128, O), dtype=torch.int32, device="cuda").permute(0, 2, 1)
     yg32 = torch.empty((m_idx.numel(), O), dtype=torch.bfloat16, device="cuda")
+    xu, sxu = torch.empty((T, I), dtype=u8, device="cuda"), fg.mn_major_scales(T, I // 128)
+    Wu, sWu = torch.empty((O, I), dtype=u8, device="cuda"), torch.empty((O // 128, I // 128), dtype=f32, device="cuda")
+    yu = torch.empty((T, O), dtype=torch.bfloat16, device="cuda")
+    xTu, sxTu = torch.empty((I, T), dtype=u8, device="cuda"), fg.mn_major_scales(I, T // 128)
+    dWu = torch.empty((I, I), dtype=f32, device="cuda")
 
     def step():
         fg.cast_per_token(x, xq, sx, 128, fg.SF_FP32)
@@ -72,9 +77,14 @@ def test_graph_replays_match_eager(gpu):
         for e in range(E):
             fg.cast_per_token(Wg[e], Wg32[e], sWg32[e], 32, fg.SF_PACKED_UE8M0)
         fg.m_grouped_gemm_fp8_nt_bf16_ue8m0_g32_contiguous(wp, swp, Wg32, sWg32, m_idx, yg32)
+        fg.cast_per_token(x, xu, sxu, 128, fg.SF_UE8M0)
+        fg.cast_per_block(W, Wu, sWu, sf_fmt=fg.SF_UE8M0)
+        fg.gemm_fp8_nt_bf16_ue8m0(xu, sxu, Wu, sWu, yu)
+        fg.cast_per_token(x.t(), xTu, sxTu, 128, fg.SF_UE8M0)
+        fg.wgrad_gemm_fp8_nt_fp32_ue8m0(xTu, sxTu, xTu, sxTu, dWu)
 
     outs = [xq, sx, xq1, sx1, wp, swp, xTq, sxT, Wq, sW, y, y1, dq, dsx, dqT, dsxT, yq, ysf, y2, W32, sW32, y32,
-            xT32, sxT32, dW32, Wgq, sWg, yg, Wg32, yg32]
+            xT32, sxT32, dW32, Wgq, sWg, yg, Wg32, yg32, xu, sxu, Wu, sWu, yu, xTu, sxTu, dWu]
 
     def snap():
         return [o.cpu().clone() for o in outs], dW.cpu().clone()
