@@ -53,11 +53,22 @@ __device__ __forceinline__ uint32_t abs_bits(float f) { return __float_as_uint(f
 //
 // A "task" is one wave-wide step over a row: 64 lanes x 16 elements = 1024
 // consecutive columns, i.e. 8 groups of 128 (8 lanes each) or 32 groups of 32
-// (2 lanes each).  Each wave walks a contiguous range of tasks (row-major
-// order), U tasks at a time so that 2*U (bf16) or 4*U (fp32) 16-byte loads per
-// lane are in flight; E4M3 bytes leave as one 16-byte store per lane.  The
-// group amax is reduced with DPP inside the 16-lane rows; packed UE8M0 words
-// are assembled with a DPP OR (group 32) or readlanes (group 128).
+// (2 lanes each).  Each wave walks a contiguous range of tasks, U tasks at a
+// time so that 2*U (bf16) or 4*U (fp32) 16-byte loads per lane are in flight;
+// E4M3 bytes leave as one 16-byte store per lane.  The group amax is reduced
+// with DPP inside the 16-lane rows; packed UE8M0 words are assembled with a
+// DPP OR (group 32) or readlanes (group 128).
+//
+// Task order.  Row-major (QUAD = false): task t is step t % steps of row
+// t / steps.  With MN-major scales (element (r, g) at g*ld + r) the U = 4 tasks
+// of a batch are instead four consecutive rows at the same column step
+// (QUAD = true), so the four scales of each group are contiguous and leave as
+// one 16-byte store, not four scattered 4-byte ones.  Hardware workgroup b runs
+// on XCD b % 8; the logical numbering puts eight consecutive workgroups (the
+// 32 rows of a 128-byte line of MN-major scales) on one XCD, so the line is
+// assembled in one L2 and reaches memory whole.  (Measured on MI355X: giving
+// each XCD one contiguous band of rows instead is 14% slower for 16384 x 4096,
+// whose bands then start 2^24 bytes apart.)
 // ---------------------------------------------------------------------------
 constexpr int kTokEl = 16;              // elements per lane per task
 constexpr int kTokSpan = 64 * kTokEl;   // columns per task
@@ -95,32 +106,47 @@ __device__ __forceinline__ void load16(const T *p, bool full, int valid, Raw16<T
   }
 }
 
-template <typename TIn, int GRAN, int FMT, bool Q16>
+template <typename TIn, int GRAN, int FMT, bool Q16, bool QUAD>
 __global__ __launch_bounds__(kThreads) void cast_tok_rows_kernel(
-    const TIn *__restrict__ x, int64_t cols, int64_t xs_row, uint8_t *__restrict__ q, int64_t q_ld,
+    const TIn *__restrict__ x, int64_t rows, int64_t cols, int64_t xs_row, uint8_t *__restrict__ q, int64_t q_ld,
     void *__restrict__ sf, int64_t sf_s_row, int64_t sf_s_grp, int64_t steps_per_row, int64_t tasks,
     int64_t tasks_per_wave) {
   constexpr int L = GRAN / kTokEl;  // lanes per group
   constexpr int U = 4;
   constexpr bool kUe8m0 = FMT != kSfFp32;
   const int lane = threadIdx.x & 63;
-  const int64_t wave = (int64_t)blockIdx.x * (kThreads / kWave) + (threadIdx.x >> 6);
+  // Within each run of 64 workgroups, logical workgroup 8i + x is hardware
+  // workgroup 8x + i, which runs on XCD i: eight consecutive logical workgroups
+  // share an XCD, and the XCDs still interleave at that grain.
+  const int64_t b = blockIdx.x;
+  const int64_t blk = (b & ~(int64_t)63) | ((b & 7) << 3) | ((b >> 3) & 7);
+  const int64_t wave = blk * (kThreads / kWave) + (threadIdx.x >> 6);
   const int64_t t_begin = wave * tasks_per_wave;
   const int64_t t_end = min(t_begin + tasks_per_wave, tasks);
 
   for (int64_t tb = t_begin; tb < t_end; tb += U) {
     Raw16<TIn> raw[U];
     int64_t row[U], col[U];
+    uint32_t sv[U];   // QUAD: the batch's scale (or packed word) per row, stored after the batch
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t t = tb + u;
       row[u] = 0;
       col[u] = cols;  // marks the lane idle
+      sv[u] = 0u;
       if (t < t_end) {
-        const int64_t r = t / steps_per_row;
-        const int64_t s = t - r * steps_per_row;
+        int64_t r, s;
+        if constexpr (QUAD) {   // tasks 4i..4i+3 of row quad R: rows 4R..4R+3 at step i
+          const int64_t quad = t / (4 * steps_per_row);
+          const int64_t rem = t - quad * 4 * steps_per_row;
+          s = rem >> 2;
+          r = 4 * quad + (rem & 3);
+        } else {
+          r = t / steps_per_row;
+          s = t - r * steps_per_row;
+        }
         row[u] = r;
-        col[u] = s * kTokSpan + (int64_t)lane * kTokEl;
+        if (r < rows) col[u] = s * kTokSpan + (int64_t)lane * kTokEl;
       }
       if (col[u] < cols) {
         load16<TIn>(x + row[u] * xs_row + col[u], col[u] + kTokEl <= cols, (int)min<int64_t>(cols - col[u], kTokEl), raw[u]);
@@ -162,7 +188,8 @@ __global__ __launch_bounds__(kThreads) void cast_tok_rows_kernel(
       }
       const int64_t g = c / GRAN;  // group of this lane
       if constexpr (FMT != kSfPackedUe8m0) {
-        if ((lane % L) == 0 && c < cols)
+        if constexpr (QUAD) sv[u] = __float_as_uint(gs.sf);
+        else if ((lane % L) == 0 && c < cols)
           reinterpret_cast<float *>(sf)[row[u] * sf_s_row + g * sf_s_grp] = gs.sf;
       } else {
         const uint32_t mine = c < cols ? gs.e8 << (8 * (g & 3)) : 0u;
@@ -177,8 +204,27 @@ __global__ __launch_bounds__(kThreads) void cast_tok_rows_kernel(
                               (uint32_t)__builtin_amdgcn_readlane((int)r16, 48);
           if (base) word = hi;
         }
-        if ((lane % (4 * L)) == 0 && c < cols)
+        if constexpr (QUAD) sv[u] = word;
+        else if ((lane % (4 * L)) == 0 && c < cols)
           reinterpret_cast<uint32_t *>(sf)[row[u] * sf_s_row + (g >> 2) * sf_s_grp] = word;
+      }
+    }
+    if constexpr (QUAD) {
+      // rows row[0] .. row[0]+3 (a multiple of 4; rows past the end were idle) at
+      // the same column: MN-major scales (s_row == 1, s_grp % 4 == 0, 16-byte
+      // aligned base) put the four values of a group side by side
+      constexpr int W = FMT == kSfPackedUe8m0 ? 4 * L : L;   // lanes per stored unit
+      const int64_t c = col[0], r0 = row[0];
+      const int64_t unit = FMT == kSfPackedUe8m0 ? c / GRAN / 4 : c / GRAN;
+      if ((lane % W) == 0 && c < cols) {
+        uint32_t *dst = reinterpret_cast<uint32_t *>(sf) + unit * sf_s_grp + r0;
+        if (r0 + 4 <= rows) {
+          *reinterpret_cast<uint4 *>(dst) = make_uint4(sv[0], sv[1], sv[2], sv[3]);
+        } else {
+#pragma unroll
+          for (int u = 0; u < U; ++u)
+            if (r0 + u < rows) dst[u] = sv[u];
+        }
       }
     }
   }
@@ -665,21 +711,28 @@ template <typename TIn, int GRAN, int FMT>
 hipError_t launch_tok_rows(const void *x, int64_t rows, int64_t cols, int64_t xs_row, uint8_t *q,
                            int64_t q_ld, void *sf, int64_t sf_s_row, int64_t sf_s_grp, hipStream_t st) {
   const int64_t steps = (cols + kTokSpan - 1) / kTokSpan;
-  const int64_t tasks = rows * steps;
+  // MN-major scales with 16-byte aligned columns of 4 rows: row-quad task order
+  const bool quad = sf_s_row == 1 && sf_s_grp % 4 == 0 && reinterpret_cast<uintptr_t>(sf) % 16 == 0 && rows > 1;
+  const int64_t tasks = quad ? (rows + 3) / 4 * 4 * steps : rows * steps;
   const int64_t target_waves = 16384;  // 16 waves per CU in flight
   int64_t tpw = (tasks + target_waves - 1) / target_waves;
   if (tpw < 1) tpw = 1;
+  if (quad) tpw = (tpw + 3) / 4 * 4;   // whole batches of one row quad
   const int64_t waves = (tasks + tpw - 1) / tpw;
-  const int64_t blocks = (waves + 3) / 4;
+  const int64_t blocks = ((waves + 3) / 4 + 63) / 64 * 64;   // whole runs of 64 workgroups
   const bool q16 = (reinterpret_cast<uintptr_t>(q) % 16 == 0) && (q_ld % 16 == 0);
-  if (q16)
-    hipLaunchKernelGGL((cast_tok_rows_kernel<TIn, GRAN, FMT, true>), dim3((unsigned)blocks), dim3(kThreads), 0, st,
-                       reinterpret_cast<const TIn *>(x), cols, xs_row, q, q_ld, sf, sf_s_row, sf_s_grp, steps, tasks,
-                       tpw);
-  else
-    hipLaunchKernelGGL((cast_tok_rows_kernel<TIn, GRAN, FMT, false>), dim3((unsigned)blocks), dim3(kThreads), 0, st,
-                       reinterpret_cast<const TIn *>(x), cols, xs_row, q, q_ld, sf, sf_s_row, sf_s_grp, steps, tasks,
-                       tpw);
+#define FGFP8_ROWS(Q, QD)                                                                                         \
+  hipLaunchKernelGGL((cast_tok_rows_kernel<TIn, GRAN, FMT, Q, QD>), dim3((unsigned)blocks), dim3(kThreads), 0, st, \
+                     reinterpret_cast<const TIn *>(x), rows, cols, xs_row, q, q_ld, sf, sf_s_row, sf_s_grp, steps, \
+                     tasks, tpw)
+  if (quad) {
+    if (q16) FGFP8_ROWS(true, true);
+    else FGFP8_ROWS(false, true);
+  } else {
+    if (q16) FGFP8_ROWS(true, false);
+    else FGFP8_ROWS(false, false);
+  }
+#undef FGFP8_ROWS
   return hipGetLastError();
 }
 

@@ -20,9 +20,10 @@ def sentinel_u8(shape, value=0xA5):
 
 
 def gpu_cast_per_token(x_cpu: torch.Tensor, gran: int, fmt: int, mn_major: bool = False,
-                       transpose: bool = False, q_pad: int = 0, sf_pad: int = 0):
+                       transpose: bool = False, q_pad: int = 0, sf_pad: int = 0, sf_align: int = 4):
     """Cast on the GPU; returns (q uint8 [rows, cols], sf as a host array [rows, units],
-    full q buffer, full sf buffer) so callers can check the untouched padding."""
+    full q buffer, full sf buffer) so callers can check the untouched padding.
+    MN-major scales use ld = align(rows + sf_pad, sf_align)."""
     x = x_cpu.cuda()
     xv = x.t() if transpose else x
     rows, cols = xv.shape
@@ -33,7 +34,7 @@ def gpu_cast_per_token(x_cpu: torch.Tensor, gran: int, fmt: int, mn_major: bool 
     qbuf = sentinel_u8((rows, q_ld))
     q = qbuf[:, :cols]
     if mn_major:
-        ld = -(-(rows + sf_pad) // 4) * 4
+        ld = -(-(rows + sf_pad) // sf_align) * sf_align
         sbuf = torch.full((units, ld), -7, dtype=torch.int32, device="cuda").view(sdt)
         sf = sbuf.t()[:rows]
     else:

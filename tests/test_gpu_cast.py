@@ -34,9 +34,9 @@ def _cast_input(shape, dtype):
     return _inputs[key]
 
 
-def _check_tok(x_cpu, gran, fmt, mn_major=False, transpose=False):
+def _check_tok(x_cpu, gran, fmt, mn_major=False, transpose=False, sf_pad=4, sf_align=4):
     q, sf, qbuf, sbuf, (q_ld, units) = gpu_cast_per_token(x_cpu, gran, fmt, mn_major, transpose, q_pad=16,
-                                                          sf_pad=4)
+                                                          sf_pad=sf_pad, sf_align=sf_align)
     oq, osf = _oracle_tok(x_cpu, gran, fmt, transpose)
     assert np.array_equal(q, oq), "E4M3 bytes differ"
     assert np.array_equal(sf, oracle_sf_bits(osf)), "scale bits differ"
@@ -74,6 +74,17 @@ def test_per_token_16384x4096(gpu, gran, fmt):
 def test_token_sweep_g32_packed(gpu, tokens):
     x = si.randn((tokens, 4096), si.SEED_A)
     _check_tok(x, 32, oracle.SF_PACKED_UE8M0, mn_major=True)
+
+
+@pytest.mark.parametrize("shape", [(7, 4096), (129, 7168), (64, 1000)])
+@pytest.mark.parametrize("gran", [32, 128])
+@pytest.mark.parametrize("fmt", FMTS, ids=["fp32", "ue8m0", "packed"])
+def test_per_token_mn_major_odd_ld(gpu, shape, gran, fmt):
+    """MN-major scales whose columns are not 16-byte aligned (ld = rows + 1): the
+    row-major task order stores each scale on its own; an aligned ld takes the
+    row-quad order with 16-byte stores of four rows (the other tests)."""
+    x = _cast_input(shape, torch.bfloat16)
+    _check_tok(x, gran, fmt, mn_major=True, sf_pad=1, sf_align=1)
 
 
 def test_ragged_columns_strided_rows(gpu):
