@@ -29,6 +29,8 @@
 //    columns of one row (8-byte bf16 stores, 16-byte fp32 read-modify-write).
 //  * Workgroups are mapped XCD by XCD onto bands of 8 m-tiles so that the
 //    tiles resident on one XCD share A and B panels in its L2.
+#include <atomic>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -790,10 +792,29 @@ hipError_t launch_gemm_g32(const GemmArgs &a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Compute units of the current device (queried once per device).
+int cu_count() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int c = cached[dev].load(std::memory_order_relaxed);
+  if (c == 0) {
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c < 1) c = 256;
+    cached[dev].store(c, std::memory_order_relaxed);
+  }
+  return c;
+}
+
 hipError_t launch_gemm(const GemmArgs &a, hipStream_t st) {
   if (!a.wgrad && a.m_idx == nullptr && a.q == nullptr && a.m <= 64) {
     // decode-sized: stream B with K split over the waves of a workgroup
     if (a.m <= 16) return launch_skinny<1, 1, 8, 4>(a, st);
+    // 16 waves (shorter K walk per wave) when the workgroups of 32 columns still
+    // fit one per CU with 16 (or 32) rows each; else 8 waves over 32 (64) rows.
+    // Measured on MI355X, m = 64, n = 4096, k = 7168: 16.5 us against 22.6 us.
+    const int64_t wn = (a.n + 31) / 32, cus = cu_count();
+    if ((a.m + 15) / 16 * wn <= cus) return launch_skinny<1, 2, 16, 2>(a, st);
+    if ((a.m + 31) / 32 * wn <= cus) return launch_skinny<2, 2, 16, 2>(a, st);
     if (a.m <= 32) return launch_skinny<2, 2, 8, 2>(a, st);
     return launch_skinny<4, 2, 8, 2>(a, st);
   }

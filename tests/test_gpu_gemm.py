@@ -150,11 +150,14 @@ def test_gemm_decode(gpu, m, nk):
 
 
 @pytest.mark.parametrize("m", [1, 5, 16, 17, 32, 33, 63, 64, 65])
-@pytest.mark.parametrize("nk", [(1000, 128), (200, 1152), (4096, 2176)])
+@pytest.mark.parametrize("nk", [(1000, 128), (200, 1152), (4096, 2176), (9000, 256), (7168, 1408)])
 def test_gemm_skinny_edges(gpu, m, nk):
     # decode-sized m: every row count around the 16 / 32 / 64-row configurations,
     # ragged n, fewer K blocks than the waves that split them (k = 128) and an
-    # uneven split (9 and 17 blocks over 8 waves)
+    # uneven split (9 and 17 blocks over 8 or 16 waves).  n = 1000 and 200 take the
+    # 16-wave 16-row configuration, n = 4096 with m > 32 the 16-wave 32-row one,
+    # n = 7168 with m > 16 the 8-wave ones (or 16-wave 32-row for m <= 32), and
+    # n = 9000 (282 column workgroups) the 8-wave ones for every m > 16.
     n, k = nk
     qa, sa, qb, sb = _cast_operands(m, n, k, scale=0.1)
     got = _run_gemm(qa, sa, qb, sb)
