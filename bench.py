@@ -13,7 +13,8 @@ in=7168, out=4096, bf16 randn inputs, 1x128 / 128x128 fp32 scales):
 `value` is the step's GEMM work (3 x 2*8192*4096*7168 flop) over the whole
 step time, casts included.  Per-kernel times come from HIP events recorded
 on the launch stream inside the timed region.  Extra kernel measurements
-(16384x4096 casts, the 1..16384-token cast sweep, prefill and decode GEMMs)
+(16384x4096 casts, the other per-token cast shapes, the 1..16384-token cast
+sweep, the 128x256x512, prefill and decode GEMMs)
 run after the timed region; `cpu_baseline` times the oracle on a bounded
 sample of the same step.
 """
@@ -280,6 +281,33 @@ def extra_kernels(fg, torch, si):
                          "graph_gbs": nbytes / (gms * 1e-3) / 1e9}
         del x, qt, sf
     out["cast_token_sweep_4096_g32_packed"] = sweep
+    # the other per-token cast shapes (with the all-zero and x1e4 groups): every group size and
+    # scale format, MN-major scales, graph-timed (these are launch-scale or L2-resident)
+    shapes = {}
+    for rows, cols in si.CAST_SHAPES[:-1]:
+        x = si.cast_workload(rows, cols).cuda()
+        qs = torch.empty((rows, cols), dtype=torch.uint8, device="cuda")
+        per = {}
+        for gran in (128, 32):
+            for fmt, fname in ((fg.SF_FP32, "fp32"), (fg.SF_UE8M0, "ue8m0"), (fg.SF_PACKED_UE8M0, "packed")):
+                G = -(-cols // gran)
+                units = -(-G // 4) if fmt == fg.SF_PACKED_UE8M0 else G
+                sf = fg.mn_major_scales(rows, units, torch.int32 if fmt == fg.SF_PACKED_UE8M0 else torch.float32)
+                gms = _time_graph(torch, lambda: fg.cast_per_token(x, qs, sf, gran, fmt))
+                nbytes = rows * cols * 3 + rows * units * 4
+                per[f"g{gran}_{fname}"] = {"graph_us": round(gms * 1e3, 2),
+                                           "graph_gbs": round(nbytes / (gms * 1e-3) / 1e9, 1)}
+        shapes[f"{rows}x{cols}"] = per
+        del x, qs
+    out["cast_per_token_shapes"] = shapes
+    # the small GEMM (m=128, n=256, k=512): launch-scale, reported in microseconds
+    m, n, k = si.GEMM_SMALL
+    A, sa, B, sb, D = _gemm_operands(fg, torch, si, m, n, k)
+    q = _time(torch, lambda: fg.gemm_fp8_nt_bf16(A, sa, B, sb, D))
+    gms = _time_graph(torch, lambda: fg.gemm_fp8_nt_bf16(A, sa, B, sb, D))
+    out[f"gemm_{m}x{n}x{k}"] = {"graph_us": gms * 1e3, "eager_us": q[0] * 1e3, "eager_p10_us": q[1] * 1e3,
+                                "eager_p90_us": q[2] * 1e3}
+    del A, sa, B, sb, D
     # prefill and decode GEMMs on randn*0.1 operands; a decode GEMM reads B once, so
     # 12 copies of B (> 256 MiB) rotate to keep it coming from HBM
     for (m, n, k) in list(si.GEMM_PREFILL) + list(si.GEMM_DECODE):
