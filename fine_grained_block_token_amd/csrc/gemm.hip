@@ -337,6 +337,26 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_kernel(GemmAr
   // or prefetching the next block into L2, does not help: the copy path's
   // bytes per clock, not its latency, is the limit with 128x128 tiles.)
   static_assert(C::kStages == 2, "two stages");
+  //
+  // B prefetch.  The XCD tile order has all eight XCDs read the same B panels in
+  // the same round of tiles, so a B that is not in the MALL (the 256 MB cache in
+  // front of HBM) stalls every XCD's copies on HBM latency in every round, which
+  // the two-stage pipeline cannot hide.  The first round of workgroups therefore
+  // reads all of B once before its K loop: 1 KB copies into stage 1 (overwritten
+  // by block 1 after the first barrier; the first wait covers them).  Measured
+  // on MI355X in the linear step: dgrad 269 -> 244 us (its B, W^T, was written
+  // long before), forward +2% (its B was just written).  The launcher enables it
+  // for forward / dgrad grids of more than one round only.
+  if (!GROUPED && (int)blockIdx.x < g.b_prefetch_wgs) {
+    const int64_t per_row = (g.k + 1023) / 1024, total = n * per_row;
+    const int64_t per_wg = (total + g.b_prefetch_wgs - 1) / g.b_prefetch_wgs;
+    const int64_t c_end = min(((int64_t)blockIdx.x + 1) * per_wg, total);
+    for (int64_t c = (int64_t)blockIdx.x * per_wg + wv; c < c_end; c += C::kWaves) {
+      const int64_t row = c / per_row;
+      const uint32_t col = (uint32_t)min((c - row * per_row) * 1024 + 16 * lane, g.k - 16);
+      load_lds16(g.B + row * g.ldb, col, smem + C::kStageBytes);
+    }
+  }
   issue(0, smem);
   for (int kb = 0; kb < KB; ++kb) {
     // wave priority 0 while waiting and issuing copies, 3 once its MFMAs run (below):
@@ -720,12 +740,31 @@ __global__ __launch_bounds__(64 * W) void gemm_skinny_kernel(GemmArgs g, int til
 
 }  // namespace
 
+// Compute units of the current device (queried once per device).
+int cu_count() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int c = cached[dev].load(std::memory_order_relaxed);
+  if (c == 0) {
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c < 1) c = 256;
+    cached[dev].store(c, std::memory_order_relaxed);
+  }
+  return c;
+}
+
 template <class C>
-hipError_t launch_cfg(const GemmArgs &a, hipStream_t st) {
-  const int tiles_m = (int)((a.m + C::kBM - 1) / C::kBM), tiles_n = (int)((a.n + C::kBN - 1) / C::kBN);
+hipError_t launch_cfg(const GemmArgs &args, hipStream_t st) {
+  const int tiles_m = (int)((args.m + C::kBM - 1) / C::kBM), tiles_n = (int)((args.n + C::kBN - 1) / C::kBN);
   const int tiles = tiles_m * tiles_n;
   const int per_xcd = (tiles + kXcds - 1) / kXcds;
   const dim3 grid((unsigned)(per_xcd * kXcds));
+  GemmArgs a = args;
+  // B prefetch for forward / dgrad grids of more than one round of tiles (the
+  // wgrad's B is twice as large and shared by fewer XCDs per round: measured
+  // 1-3% slower with it, as is a one-round grid)
+  const int64_t first_round = (int64_t)C::kMinBlocks * cu_count();
+  a.b_prefetch_wgs = (!a.wgrad && grid.x > first_round) ? (int)first_round : 0;
 #define FGFP8_GEMM(SAF, WG, GR, CF) \
   hipLaunchKernelGGL((gemm_kernel<C, SAF, WG, GR, CF>), grid, dim3(C::kThreads), 0, st, a, tiles_m, tiles_n)
   const bool packed = a.sa_fmt == kSfPackedUe8m0;
@@ -790,19 +829,6 @@ hipError_t launch_gemm_g32(const GemmArgs &a, hipStream_t st) {
   else
     hipLaunchKernelGGL((gemm_g32_kernel<C, false, false>), grid, dim3(C::kThreads), 0, st, a, tiles_m, tiles_n);
   return hipGetLastError();
-}
-
-// Compute units of the current device (queried once per device).
-int cu_count() {
-  static std::atomic<int> cached[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  int c = cached[dev].load(std::memory_order_relaxed);
-  if (c == 0) {
-    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c < 1) c = 256;
-    cached[dev].store(c, std::memory_order_relaxed);
-  }
-  return c;
 }
 
 hipError_t launch_gemm(const GemmArgs &a, hipStream_t st) {

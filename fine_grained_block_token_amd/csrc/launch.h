@@ -86,6 +86,9 @@ struct GemmArgs {
   // (packed words) or 128 (wgrad only: packed words, or fp32 2^e values when
   // sa_fmt is kSfUe8m0).
   int ue_gran = 32;
+  // Workgroups (blockIdx.x below this) that first read all of B through the
+  // caches, so that later rounds of tiles find it in the MALL; 0: none.
+  int b_prefetch_wgs = 0;
 };
 
 hipError_t launch_cast_per_token(const CastTokenArgs &a, hipStream_t st);
