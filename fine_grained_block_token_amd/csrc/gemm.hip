@@ -551,6 +551,17 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_g32_kernel(Ge
   // (packed group 128, below) the block's byte of its word
   auto shift0 = [&](int mode) { return mode == kUeG32Packed ? 8 * (lane >> 4) : mode == kUeG128Packed ? 0 : 23; };
   const int gsh_a0 = shift0(SMODE), gsh_b0 = shift0(SB_MODE);
+  // B prefetch of the first round of workgroups, as in gemm_kernel
+  if (!GROUPED && (int)blockIdx.x < g.b_prefetch_wgs) {
+    const int64_t per_row = (g.k + 1023) / 1024, total = n * per_row;
+    const int64_t per_wg = (total + g.b_prefetch_wgs - 1) / g.b_prefetch_wgs;
+    const int64_t c_end = min(((int64_t)blockIdx.x + 1) * per_wg, total);
+    for (int64_t c = (int64_t)blockIdx.x * per_wg + wv; c < c_end; c += C::kWaves) {
+      const int64_t row = c / per_row;
+      const uint32_t col = (uint32_t)min((c - row * per_row) * 1024 + 16 * lane, g.k - 16);
+      load_lds16(g.B + row * g.ldb, col, smem + C::kStageBytes);
+    }
+  }
   issue(0, smem);
   for (int kb = 0; kb < KB; ++kb) {
     asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier\n\ts_setprio 0" ::: "memory");
@@ -803,11 +814,14 @@ hipError_t launch_skinny(const GemmArgs &a, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_g32(const GemmArgs &a, hipStream_t st) {
+hipError_t launch_gemm_g32(const GemmArgs &args, hipStream_t st) {
   using C = Cfg<2, 2, 2>;
-  const int tiles_m = (int)((a.m + C::kBM - 1) / C::kBM), tiles_n = (int)((a.n + C::kBN - 1) / C::kBN);
+  const int tiles_m = (int)((args.m + C::kBM - 1) / C::kBM), tiles_n = (int)((args.n + C::kBN - 1) / C::kBN);
   const int per_xcd = (tiles_m * tiles_n + kXcds - 1) / kXcds;
   const dim3 grid((unsigned)(per_xcd * kXcds));
+  GemmArgs a = args;   // B prefetch: forward / dgrad grids of more than one round
+  const int64_t first_round = (int64_t)C::kMinBlocks * cu_count();
+  a.b_prefetch_wgs = (!a.wgrad && grid.x > first_round) ? (int)first_round : 0;
   if (a.wgrad && a.ue_gran == 128)   // UE8M0 1x128 scales on both operands
     if (a.sa_fmt == kSfPackedUe8m0)
       hipLaunchKernelGGL((gemm_g32_kernel<C, true, false, kUeG128Packed>), grid, dim3(C::kThreads), 0, st, a, tiles_m,
