@@ -135,6 +135,26 @@ __device__ __forceinline__ void load_lds4(const void *base, uint32_t off, uint8_
                ::"v"(off), "s"(base), "s"(lds) : "memory", "m0");
 }
 
+// B prefetch of one workgroup of the first round (blockIdx.x < b_prefetch_wgs):
+// its share of B's 1 KB row chunks, up to kPrefetch copies per wave (64 KB per
+// workgroup; chunks past the share repeat its last one), into the 1 KB slot
+// `junk`.  Exactly kPrefetch copies per wave, so the first wait can count them.
+constexpr int kPrefetch = 16;
+template <class C>
+__device__ __forceinline__ void b_prefetch(const GemmArgs &g, int64_t n, int wv, int lane, uint8_t *junk) {
+  const int64_t per_row = (g.k + 1023) / 1024, total = n * per_row;   // total >= 1
+  const int64_t per_wg = (total + g.b_prefetch_wgs - 1) / g.b_prefetch_wgs;
+  const int64_t c_first = (int64_t)blockIdx.x * per_wg;
+  const int64_t c_last = min(c_first + per_wg, total) - 1;   // may lie below c_first: then the last chunk
+#pragma unroll
+  for (int j = 0; j < kPrefetch; ++j) {
+    const int64_t c = min(c_first + wv + (int64_t)j * C::kWaves, c_last);
+    const int64_t row = c / per_row;
+    const uint32_t col = (uint32_t)min((c - row * per_row) * 1024 + 16 * lane, g.k - 16);
+    load_lds16(g.B + row * g.ldb, col, junk);
+  }
+}
+
 // acc += P * scale for MFMA tile (mi, ni)
 template <bool WGRAD>
 __device__ __forceinline__ void promote(v4f &acc, const v4f &p, const BlockScales &s, int mi, int ni) {
@@ -211,7 +231,8 @@ __device__ __forceinline__ void fused_cast_epilogue(const GemmArgs &g, const v4f
 
 template <class C, int SA_FMT, bool WGRAD, bool GROUPED, int CASTF>
 __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_kernel(GemmArgs g, int tiles_m, int tiles_n) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::kStages * C::kStageBytes];
+  // the stages, then a 1 KB slot that receives the B prefetch copies
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::kStages * C::kStageBytes + 1024];
   const int t = threadIdx.x, lane = t & 63;
   const int wv = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wm = (wv / C::WAVES_N_) * 64, wn = (wv % C::WAVES_N_) * 64;
@@ -342,26 +363,23 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_kernel(GemmAr
   // the same round of tiles, so a B that is not in the MALL (the 256 MB cache in
   // front of HBM) stalls every XCD's copies on HBM latency in every round, which
   // the two-stage pipeline cannot hide.  The first round of workgroups therefore
-  // reads all of B once before its K loop: 1 KB copies into stage 1 (overwritten
-  // by block 1 after the first barrier; the first wait covers them).  Measured
-  // on MI355X in the linear step: dgrad 269 -> 244 us (its B, W^T, was written
-  // long before), forward +2% (its B was just written).  The launcher enables it
-  // for forward / dgrad grids of more than one round only.
-  if (!GROUPED && (int)blockIdx.x < g.b_prefetch_wgs) {
-    const int64_t per_row = (g.k + 1023) / 1024, total = n * per_row;
-    const int64_t per_wg = (total + g.b_prefetch_wgs - 1) / g.b_prefetch_wgs;
-    const int64_t c_end = min(((int64_t)blockIdx.x + 1) * per_wg, total);
-    for (int64_t c = (int64_t)blockIdx.x * per_wg + wv; c < c_end; c += C::kWaves) {
-      const int64_t row = c / per_row;
-      const uint32_t col = (uint32_t)min((c - row * per_row) * 1024 + 16 * lane, g.k - 16);
-      load_lds16(g.B + row * g.ldb, col, smem + C::kStageBytes);
-    }
-  }
+  // reads B once (b_prefetch: its share of up to 64 KB per workgroup) right after
+  // block 0's copies: kPrefetch 1 KB copies per wave into the spare LDS slot.
+  // Copies complete in order, so the first wait lets exactly those be in flight
+  // and block 0's MFMAs overlap them.  Measured on MI355X in the linear step
+  // (20 steps back to back): dgrad 291 -> 273 us (its B, W^T, was written long
+  // before), forward +1%, step -1.4%.  The launcher enables it for forward /
+  // dgrad grids of more than one round only.
   issue(0, smem);
+  const bool prefetching = !GROUPED && (int)blockIdx.x < g.b_prefetch_wgs;
+  if (prefetching) b_prefetch<C>(g, n, wv, lane, smem + C::kStages * C::kStageBytes);
   for (int kb = 0; kb < KB; ++kb) {
     // wave priority 0 while waiting and issuing copies, 3 once its MFMAs run (below):
     // the SIMD's other wave, if it is in its MFMA phase, is served first
-    asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier\n\ts_setprio 0" ::: "memory");
+    if (prefetching && kb == 0)   // block 0 has landed; the prefetch copies may be in flight
+      asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier\n\ts_setprio 0" ::"n"(kPrefetch) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier\n\ts_setprio 0" ::: "memory");
     const uint8_t *st = smem + (kb & 1) * C::kStageBytes;
     // The copy into the free stage goes first: inline assembly bounds the
     // scheduling region, and the fragment reads must share one with the MFMAs.
@@ -472,7 +490,8 @@ enum : int { kUeG32Packed = 0, kUeG128Packed = 1, kUeG128Float = 2, kUeBlockFloa
 
 template <class C, bool WGRAD, bool GROUPED, int SMODE = kUeG32Packed, int SB_MODE = SMODE>
 __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_g32_kernel(GemmArgs g, int tiles_m, int tiles_n) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::kStages * C::kStageBytes];
+  // the stages, then a 1 KB slot that receives the B prefetch copies
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::kStages * C::kStageBytes + 1024];
   const int t = threadIdx.x, lane = t & 63;
   const int wv = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wm = (wv / C::WAVES_N_) * 64, wn = (wv % C::WAVES_N_) * 64;
@@ -551,20 +570,15 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_g32_kernel(Ge
   // (packed group 128, below) the block's byte of its word
   auto shift0 = [&](int mode) { return mode == kUeG32Packed ? 8 * (lane >> 4) : mode == kUeG128Packed ? 0 : 23; };
   const int gsh_a0 = shift0(SMODE), gsh_b0 = shift0(SB_MODE);
-  // B prefetch of the first round of workgroups, as in gemm_kernel
-  if (!GROUPED && (int)blockIdx.x < g.b_prefetch_wgs) {
-    const int64_t per_row = (g.k + 1023) / 1024, total = n * per_row;
-    const int64_t per_wg = (total + g.b_prefetch_wgs - 1) / g.b_prefetch_wgs;
-    const int64_t c_end = min(((int64_t)blockIdx.x + 1) * per_wg, total);
-    for (int64_t c = (int64_t)blockIdx.x * per_wg + wv; c < c_end; c += C::kWaves) {
-      const int64_t row = c / per_row;
-      const uint32_t col = (uint32_t)min((c - row * per_row) * 1024 + 16 * lane, g.k - 16);
-      load_lds16(g.B + row * g.ldb, col, smem + C::kStageBytes);
-    }
-  }
   issue(0, smem);
+  // B prefetch of the first round of workgroups, as in gemm_kernel
+  const bool prefetching = !GROUPED && (int)blockIdx.x < g.b_prefetch_wgs;
+  if (prefetching) b_prefetch<C>(g, n, wv, lane, smem + C::kStages * C::kStageBytes);
   for (int kb = 0; kb < KB; ++kb) {
-    asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier\n\ts_setprio 0" ::: "memory");
+    if (prefetching && kb == 0)   // block 0 has landed; the prefetch copies may be in flight
+      asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier\n\ts_setprio 0" ::"n"(kPrefetch) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier\n\ts_setprio 0" ::: "memory");
     const uint8_t *st = smem + (kb & 1) * C::kStageBytes;
     if (kb + 1 < KB) issue(kb + 1, smem + ((kb + 1) & 1) * C::kStageBytes);
     const int gsh_a = SMODE == kUeG128Packed ? 8 * (kb & 3) : gsh_a0;
