@@ -833,9 +833,11 @@ hipError_t launch_gemm_g32(const GemmArgs &args, hipStream_t st) {
   const int tiles_m = (int)((args.m + C::kBM - 1) / C::kBM), tiles_n = (int)((args.n + C::kBN - 1) / C::kBN);
   const int per_xcd = (tiles_m * tiles_n + kXcds - 1) / kXcds;
   const dim3 grid((unsigned)(per_xcd * kXcds));
-  GemmArgs a = args;   // B prefetch: forward / dgrad grids of more than one round
+  // B prefetch for grids of more than one round (here the weight gradient too:
+  // measured in the group-32 step, wgrad 298 -> 289 us)
+  GemmArgs a = args;
   const int64_t first_round = (int64_t)C::kMinBlocks * cu_count();
-  a.b_prefetch_wgs = (!a.wgrad && grid.x > first_round) ? (int)first_round : 0;
+  a.b_prefetch_wgs = grid.x > first_round ? (int)first_round : 0;
   if (a.wgrad && a.ue_gran == 128)   // UE8M0 1x128 scales on both operands
     if (a.sa_fmt == kSfPackedUe8m0)
       hipLaunchKernelGGL((gemm_g32_kernel<C, true, false, kUeG128Packed>), grid, dim3(C::kThreads), 0, st, a, tiles_m,
