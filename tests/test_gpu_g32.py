@@ -45,8 +45,10 @@ def _run(qa, wa, qb, wb):
 
 
 @pytest.mark.parametrize("mnk", [(128, 256, 512), (1, 128, 128), (129, 200, 256), (257, 130, 640),
-                                 (64, 1000, 1024), (256, 384, 7168)])
+                                 (64, 1000, 1024), (256, 384, 7168), (128 * 600, 100, 128)])
 def test_g32_full_compare(gpu, mnk):
+    # the last shape: 600 tiles in one column, more than one round, so the first
+    # round reads B (100 one-chunk rows) ahead of its K loop
     qa, wa, qb, wb = _operands(*mnk)
     k = mnk[2]
     sa, sb = oracle.unpack_ue8m0(wa, k // 32), oracle.unpack_ue8m0(wb, k // 32)
@@ -122,7 +124,8 @@ def _check_wgrad(got, ref, absum, trunc, k, what):
     print(f"[wgrad-g32-parity] {what}: relative Frobenius {rel:.3e}", flush=True)
 
 
-@pytest.mark.parametrize("shape", [(256, 512, 1024), (384, 130, 200), (1024, 256, 128), (384, 250, 38360)])
+@pytest.mark.parametrize("shape", [(256, 512, 1024), (384, 130, 200), (1024, 256, 128), (384, 250, 38360),
+                                   (128, 128 * 600, 100)])
 def test_wgrad_g32_full_compare(gpu, shape):
     tokens, d_out, d_in = shape
     qa, wa, qb, wb = _wgrad_operands(tokens, d_out, d_in)

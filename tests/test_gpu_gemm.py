@@ -206,6 +206,17 @@ def test_gemm_many_ragged_tiles(gpu):
                     f"gemm many ragged tiles {_MANY_MNK}")
 
 
+def test_gemm_tall_thin_many_tiles(gpu):
+    # 600 tiles in one column of tiles: more than one round, so the first round
+    # reads B ahead of its K loop, and B (100 rows of one 1 KB chunk) is smaller
+    # than the 512 shares of that read (most workgroups repeat its last chunk)
+    m, n, k = 128 * 600, 100, 128
+    qa, sa, qb, sb = _cast_operands(m, n, k)
+    got = _run_gemm(qa, sa, qb, sb)
+    ref, absum = oracle.gemm_nt(qa, sa, qb, sb)
+    check_bf16_gemm(got, ref, absum, mfma_truncation_bound(qa, sa, qb, sb), k // 128, f"gemm tall thin {(m, n, k)}")
+
+
 def test_gemm_many_ragged_tiles_packed_ue8m0(gpu):
     qa, words, qb, sb = _cast_operands(*_MANY_MNK, a_fmt=oracle.SF_PACKED_UE8M0)
     sa = oracle.unpack_ue8m0(words, _MANY_MNK[2] // 128)
