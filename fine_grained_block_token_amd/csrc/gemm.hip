@@ -29,6 +29,10 @@
 //    columns of one row (8-byte bf16 stores, 16-byte fp32 read-modify-write).
 //  * Workgroups are mapped XCD by XCD onto bands of 8 m-tiles so that the
 //    tiles resident on one XCD share A and B panels in its L2.
+//  * Operands that are not in the MALL stall the copies on HBM latency, which
+//    the two stages cannot hide: the first round of workgroups reads all of B
+//    once, and each weight-gradient tile reads its D, right after block 0's
+//    copies (overlapped with block 0's MFMAs).
 #include <atomic>
 
 #include "device_common.h"
@@ -250,7 +254,8 @@ __device__ __forceinline__ void fused_cast_epilogue(const GemmArgs &g, const v4f
 
 template <class C, int SA_FMT, bool WGRAD, bool GROUPED, int CASTF>
 __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_kernel(GemmArgs g, int tiles_m, int tiles_n) {
-  // the stages, then a 1 KB slot that receives the B prefetch copies
+  // the stages, then a 1 KB slot that receives the prefetch copies (B, or a
+  // weight-gradient tile's D)
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::kStages * C::kStageBytes + 1024];
   const int t = threadIdx.x, lane = t & 63;
   const int wv = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -514,7 +519,8 @@ enum : int { kUeG32Packed = 0, kUeG128Packed = 1, kUeG128Float = 2, kUeBlockFloa
 
 template <class C, bool WGRAD, bool GROUPED, int SMODE = kUeG32Packed, int SB_MODE = SMODE>
 __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_g32_kernel(GemmArgs g, int tiles_m, int tiles_n) {
-  // the stages, then a 1 KB slot that receives the B prefetch copies
+  // the stages, then a 1 KB slot that receives the prefetch copies (B, or a
+  // weight-gradient tile's D)
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::kStages * C::kStageBytes + 1024];
   const int t = threadIdx.x, lane = t & 63;
   const int wv = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -793,7 +799,7 @@ __global__ __launch_bounds__(64 * W) void gemm_skinny_kernel(GemmArgs g, int til
 }  // namespace
 
 // Compute units of the current device (queried once per device).
-int cu_count() {
+static int cu_count() {
   static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
