@@ -144,7 +144,7 @@ def cast_per_block(x: torch.Tensor, q: torch.Tensor, sf: torch.Tensor, qT: torch
 
 def cast_per_token_dual(x: torch.Tensor, q: torch.Tensor, sf: torch.Tensor, qT: torch.Tensor,
                         sfT: torch.Tensor, sf_fmt: int = SF_FP32, gran_k: int = 128) -> None:
-    """Both 1 x gran_k per-token casts of row-major bf16 ``x`` [rows, cols] from one read:
+    """Both 1 x gran_k per-token casts of row-major bf16 or fp32 ``x`` [rows, cols] from one read:
     ``q``/``sf`` as cast_per_token(x, gran_k, sf_fmt) and ``qT`` [cols, rows] / ``sfT`` as
     cast_per_token(x.t(), gran_k, sf_fmt) (float scales, or int32 packed-UE8M0 words)."""
     q, qT = _u8(q), _u8(qT)

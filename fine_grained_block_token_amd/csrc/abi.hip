@@ -111,13 +111,14 @@ int cast_per_token_dual(const void *x, int x_dtype, int64_t rows, int64_t cols, 
                         int sf_fmt, uint8_t *q, int64_t q_ld, void *sf, int64_t sf_stride_row,
                         int64_t sf_stride_group, uint8_t *qT, int64_t qT_ld, void *sfT, int64_t sfT_stride_row,
                         int64_t sfT_stride_group, void *stream) {
-  if (x_dtype != kInBf16) return FGFP8_EINVAL;
+  if (x_dtype != kInBf16 && x_dtype != kInFp32) return FGFP8_EINVAL;
   if (gran_k != 32 && gran_k != 128) return FGFP8_EINVAL;
   if (sf_fmt != kSfFp32 && sf_fmt != kSfUe8m0 && sf_fmt != kSfPackedUe8m0) return FGFP8_EINVAL;
   if (rows < 0 || cols < 0) return FGFP8_EINVAL;
   if (rows == 0 || cols == 0) return FGFP8_OK;
   if (!x || !q || !sf || !qT || !sfT) return FGFP8_EINVAL;
-  if (!aligned(x, 16) || x_ld < cols || x_ld % 8 != 0) return FGFP8_EINVAL;
+  const int64_t es = x_dtype == kInBf16 ? 2 : 4;
+  if (!aligned(x, 16) || x_ld < cols || (x_ld * es) % 16 != 0) return FGFP8_EINVAL;
   if (!aligned(q, 8) || q_ld < cols || q_ld % 8 != 0) return FGFP8_EINVAL;
   if (!aligned(qT, 16) || qT_ld < rows || qT_ld % 16 != 0) return FGFP8_EINVAL;
   if (!aligned(sf, 4) || !aligned(sfT, 4)) return FGFP8_EINVAL;
@@ -130,8 +131,8 @@ int cast_per_token_dual(const void *x, int x_dtype, int64_t rows, int64_t cols, 
   if (cdiv(rows, 128) * cdiv(cols, 128) > 0x7FFFFFFF) return FGFP8_EINVAL;
   const int dev = check_device();
   if (dev != FGFP8_OK) return dev;
-  fgfp8::CastDualArgs a{x, rows, cols, x_ld, gran_k, sf_fmt, q, q_ld, sf, sf_stride_row, sf_stride_group,
-                        qT, qT_ld, sfT, sfT_stride_row, sfT_stride_group};
+  fgfp8::CastDualArgs a{x, x_dtype, rows, cols, x_ld, gran_k, sf_fmt, q, q_ld, sf, sf_stride_row,
+                        sf_stride_group, qT, qT_ld, sfT, sfT_stride_row, sfT_stride_group};
   return launched(fgfp8::launch_cast_dual(a, static_cast<hipStream_t>(stream)));
 }
 

@@ -118,8 +118,9 @@ __global__ __launch_bounds__(kThreads) void cast_tok_rows_kernel(
   // Within each run of 64 workgroups, logical workgroup 8i + x is hardware
   // workgroup 8x + i, which runs on XCD i: eight consecutive logical workgroups
   // share an XCD, and the XCDs still interleave at that grain.
+  // (a grid of fewer than 64 workgroups keeps the hardware order)
   const int64_t b = blockIdx.x;
-  const int64_t blk = (b & ~(int64_t)63) | ((b & 7) << 3) | ((b >> 3) & 7);
+  const int64_t blk = gridDim.x < 64 ? b : (b & ~(int64_t)63) | ((b & 7) << 3) | ((b >> 3) & 7);
   const int64_t wave = blk * (kThreads / kWave) + (threadIdx.x >> 6);
   const int64_t t_begin = wave * tasks_per_wave;
   const int64_t t_end = min(t_begin + tasks_per_wave, tasks);
@@ -520,6 +521,8 @@ __global__ __launch_bounds__(kThreads) void cast_block_kernel(
 // unused bytes.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int dual_word(int f, int v) { return f * 64 + (v ^ (4 * (((f >> 3) ^ (f & 3)) & 15))); }
+// fp32 input: one row per word, 128 words per column, the same key at 16-byte grain
+__device__ __forceinline__ int dual_word32(int f, int r) { return f * 128 + (r ^ (4 * (((f >> 3) ^ (f & 3)) & 15))); }
 
 template <int FMT>
 __device__ __forceinline__ void store_scale(void *sf, int64_t idx, const GroupScale &gs) {
@@ -535,15 +538,17 @@ __device__ __forceinline__ void store_packed_byte(void *sf, int64_t row_off, int
     for (int b = (int)(g & 3) + 1; b < 4; ++b) w[b] = 0;
 }
 
-template <int GRAN, int FMT>
+template <typename TIn, int GRAN, int FMT>
 __global__ __launch_bounds__(kThreads) void cast_dual_kernel(
-    const uint16_t *__restrict__ x, int64_t rows, int64_t cols, int64_t ld, int64_t tiles_c,
+    const TIn *__restrict__ x, int64_t rows, int64_t cols, int64_t ld, int64_t tiles_c,
     uint8_t *__restrict__ q, int64_t q_ld, void *__restrict__ sf, int64_t sf_s_row, int64_t sf_s_grp,
     uint8_t *__restrict__ qT, int64_t qT_ld, void *__restrict__ sfT, int64_t sfT_s_row, int64_t sfT_s_grp) {
   static_assert(GRAN == 32 || GRAN == 128, "group 32 or 128");
   constexpr bool UE8M0 = FMT != kSfFp32;
   constexpr bool PACKED = FMT == kSfPackedUe8m0;
-  __shared__ __attribute__((aligned(16))) uint32_t tile[128 * 64];
+  constexpr bool F32 = sizeof(TIn) == 4;   // fp32 input: 8 words per 8 columns, one row per LDS word
+  constexpr int W = F32 ? 8 : 4;
+  __shared__ __attribute__((aligned(16))) uint32_t tile[F32 ? 128 * 128 : 128 * 64];
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const int64_t r0 = (int64_t)(blockIdx.x / tiles_c) * 128, c0 = (int64_t)(blockIdx.x % tiles_c) * 128;
   const int c = lane & 15, j = lane >> 4;
@@ -551,26 +556,34 @@ __global__ __launch_bounds__(kThreads) void cast_dual_kernel(
   const int validf = (int)max<int64_t>(0, min<int64_t>(8, cols - fc));
   const int64_t G = (cols + GRAN - 1) / GRAN, GT = (rows + GRAN - 1) / GRAN;   // groups per row / column
 
-  uint32_t raw[4][2][4];
+  uint32_t raw[4][2][W];   // bf16: column pairs; fp32: one column per word
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const int64_t r = r0 + 32 * wv + 2 * (4 * i + j) + s;
-      uint32_t w[4] = {0u, 0u, 0u, 0u};
+      uint32_t w[W];
+#pragma unroll
+      for (int k = 0; k < W; ++k) w[k] = 0u;
       if (r < rows && validf > 0) {
-        const uint16_t *p = x + r * ld + fc;
+        const TIn *p = x + r * ld + fc;
         if (validf == 8) {
-          const uint4 v = *reinterpret_cast<const uint4 *>(p);
-          w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+#pragma unroll
+          for (int h = 0; h < W / 4; ++h) {
+            const uint4 v = reinterpret_cast<const uint4 *>(p)[h];
+            w[4 * h] = v.x; w[4 * h + 1] = v.y; w[4 * h + 2] = v.z; w[4 * h + 3] = v.w;
+          }
         } else {
 #pragma unroll
           for (int e = 0; e < 8; ++e)
-            if (e < validf) w[e >> 1] |= (uint32_t)p[e] << (16 * (e & 1));
+            if (e < validf) {
+              if constexpr (F32) w[e] = __float_as_uint(p[e]);
+              else w[e >> 1] |= (uint32_t)p[e] << (16 * (e & 1));
+            }
         }
       }
 #pragma unroll
-      for (int k = 0; k < 4; ++k) raw[i][s][k] = w[k];
+      for (int k = 0; k < W; ++k) raw[i][s][k] = w[k];
     }
 
   // rows: 1 x GRAN groups along the tile row (16 lanes x 8 columns, or 4 lanes per group)
@@ -580,7 +593,10 @@ __global__ __launch_bounds__(kThreads) void cast_dual_kernel(
     for (int s = 0; s < 2; ++s) {
       float v[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = (e & 1) ? bf16_hi(raw[i][s][e >> 1]) : bf16_lo(raw[i][s][e >> 1]);
+      for (int e = 0; e < 8; ++e) {
+        if constexpr (F32) v[e] = __uint_as_float(raw[i][s][e]);
+        else v[e] = (e & 1) ? bf16_hi(raw[i][s][e >> 1]) : bf16_lo(raw[i][s][e >> 1]);
+      }
       uint32_t am = 0;
 #pragma unroll
       for (int e = 0; e < 8; ++e) am = max(am, abs_bits(v[e]));
@@ -615,15 +631,21 @@ __global__ __launch_bounds__(kThreads) void cast_dual_kernel(
       }
     }
 
-  // transpose through LDS: word (col f, pair v) = bf16 of rows 2v (low) and 2v+1 (high)
+  // transpose through LDS: bf16, word (col f, pair v) = rows 2v (low) and 2v+1 (high);
+  // fp32, word (col f, row r)
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int v = 16 * wv + 4 * i + j;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const uint32_t lo = (raw[i][0][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-      const uint32_t hi = (raw[i][1][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-      tile[dual_word(8 * c + e, v)] = lo | (hi << 16);
+      if constexpr (F32) {
+        tile[dual_word32(8 * c + e, 2 * v)] = raw[i][0][e];
+        tile[dual_word32(8 * c + e, 2 * v + 1)] = raw[i][1][e];
+      } else {
+        const uint32_t lo = (raw[i][0][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+        const uint32_t hi = (raw[i][1][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+        tile[dual_word(8 * c + e, v)] = lo | (hi << 16);
+      }
     }
   }
   __syncthreads();
@@ -633,17 +655,26 @@ __global__ __launch_bounds__(kThreads) void cast_dual_kernel(
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
     const int fl = (t >> 2) + 64 * half;
-    uint32_t wd[16];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint4 a = *reinterpret_cast<const uint4 *>(&tile[dual_word(fl, 16 * p + 4 * k)]);
-      wd[4 * k] = a.x; wd[4 * k + 1] = a.y; wd[4 * k + 2] = a.z; wd[4 * k + 3] = a.w;
-    }
     float v[32];
+    if constexpr (F32) {
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      v[2 * k] = bf16_lo(wd[k]);
-      v[2 * k + 1] = bf16_hi(wd[k]);
+      for (int k = 0; k < 8; ++k) {
+        const uint4 a = *reinterpret_cast<const uint4 *>(&tile[dual_word32(fl, 32 * p + 4 * k)]);
+        v[4 * k] = __uint_as_float(a.x); v[4 * k + 1] = __uint_as_float(a.y);
+        v[4 * k + 2] = __uint_as_float(a.z); v[4 * k + 3] = __uint_as_float(a.w);
+      }
+    } else {
+      uint32_t wd[16];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint4 a = *reinterpret_cast<const uint4 *>(&tile[dual_word(fl, 16 * p + 4 * k)]);
+        wd[4 * k] = a.x; wd[4 * k + 1] = a.y; wd[4 * k + 2] = a.z; wd[4 * k + 3] = a.w;
+      }
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        v[2 * k] = bf16_lo(wd[k]);
+        v[2 * k + 1] = bf16_hi(wd[k]);
+      }
     }
     uint32_t am = 0;
 #pragma unroll
@@ -724,7 +755,10 @@ hipError_t launch_tok_rows(const void *x, int64_t rows, int64_t cols, int64_t xs
   if (tpw < 1) tpw = 1;
   if (quad) tpw = (tpw + 3) / 4 * 4;   // whole batches of one row quad
   const int64_t waves = (tasks + tpw - 1) / tpw;
-  const int64_t blocks = ((waves + 3) / 4 + 63) / 64 * 64;   // whole runs of 64 workgroups
+  // whole runs of 64 workgroups for the XCD-grouped numbering; a small cast
+  // launches only the workgroups it needs
+  const int64_t wgs = (waves + 3) / 4;
+  const int64_t blocks = wgs < 64 ? wgs : (wgs + 63) / 64 * 64;
   const bool q16 = (reinterpret_cast<uintptr_t>(q) % 16 == 0) && (q_ld % 16 == 0);
 #define FGFP8_ROWS(Q, QD)                                                                                         \
   hipLaunchKernelGGL((cast_tok_rows_kernel<TIn, GRAN, FMT, Q, QD>), dim3((unsigned)blocks), dim3(kThreads), 0, st, \
@@ -784,20 +818,26 @@ hipError_t launch_cast_per_token(const CastTokenArgs &a, hipStream_t st) {
 hipError_t launch_cast_dual(const CastDualArgs &a, hipStream_t st) {
   const int64_t tiles_c = (a.cols + 127) / 128, tiles = tiles_c * ((a.rows + 127) / 128);
   const dim3 grid((unsigned)tiles);
-  const uint16_t *x = reinterpret_cast<const uint16_t *>(a.x);
-#define FGFP8_DUAL(GR, F)                                                                                    \
-  hipLaunchKernelGGL((cast_dual_kernel<GR, F>), grid, dim3(kThreads), 0, st, x, a.rows, a.cols, a.x_ld, tiles_c, \
-                     a.q, a.q_ld, a.sf, a.sf_stride_row, a.sf_stride_group, a.qT, a.qT_ld, a.sfT,              \
-                     a.sfT_stride_row, a.sfT_stride_group)
-  if (a.gran_k == 32) {
-    if (a.sf_fmt == kSfPackedUe8m0) FGFP8_DUAL(32, kSfPackedUe8m0);
-    else if (a.sf_fmt == kSfUe8m0) FGFP8_DUAL(32, kSfUe8m0);
-    else FGFP8_DUAL(32, kSfFp32);
-  } else {
-    if (a.sf_fmt == kSfPackedUe8m0) FGFP8_DUAL(128, kSfPackedUe8m0);
-    else if (a.sf_fmt == kSfUe8m0) FGFP8_DUAL(128, kSfUe8m0);
-    else FGFP8_DUAL(128, kSfFp32);
+#define FGFP8_DUAL(T, GR, F)                                                                                  \
+  hipLaunchKernelGGL((cast_dual_kernel<T, GR, F>), grid, dim3(kThreads), 0, st, reinterpret_cast<const T *>(a.x), \
+                     a.rows, a.cols, a.x_ld, tiles_c, a.q, a.q_ld, a.sf, a.sf_stride_row, a.sf_stride_group, a.qT,   \
+                     a.qT_ld, a.sfT, a.sfT_stride_row, a.sfT_stride_group)
+#define FGFP8_DUAL_FMT(T)                                                   \
+  if (a.gran_k == 32) {                                                     \
+    if (a.sf_fmt == kSfPackedUe8m0) FGFP8_DUAL(T, 32, kSfPackedUe8m0);      \
+    else if (a.sf_fmt == kSfUe8m0) FGFP8_DUAL(T, 32, kSfUe8m0);             \
+    else FGFP8_DUAL(T, 32, kSfFp32);                                        \
+  } else {                                                                  \
+    if (a.sf_fmt == kSfPackedUe8m0) FGFP8_DUAL(T, 128, kSfPackedUe8m0);     \
+    else if (a.sf_fmt == kSfUe8m0) FGFP8_DUAL(T, 128, kSfUe8m0);            \
+    else FGFP8_DUAL(T, 128, kSfFp32);                                       \
   }
+  if (a.x_dtype == kInFp32) {
+    FGFP8_DUAL_FMT(float)
+  } else {
+    FGFP8_DUAL_FMT(uint16_t)
+  }
+#undef FGFP8_DUAL_FMT
 #undef FGFP8_DUAL
   return hipGetLastError();
 }

@@ -2,21 +2,22 @@
 //
 // D = (A * sa)(B * sb)^T, A [m, k] and B [n, k] E4M3 row-major ("DeepGEMM
 // Essentials: High-Performance FP8 Matrix Multiplication", Parts 1 and 6).
-// For every 128-wide K block one V_MFMA_SCALE_F32_16X16X128_F8F6F4 (neutral
-// hardware scales) per 16x16 output tile produces that block's partial sum,
-// which is then promoted into an fp32 register accumulator with the
-// fine-grained scales: sa(i, kb) * sb(j/128, kb) for forward/dgrad (one RHS
-// scale per 128x128 block, whose row of ceil(k/128) values serves every K
-// block -- the reply in "[Help] Starter script for nn.Linear for fwd,bwd"),
-// or sa(i, kb) * sb(j, kb) for wgrad ("DeepGEMM Essentials", Parts 12-13:
-// fp32 output, accumulated in place).
+// Forward / dgrad: for every 128-wide K block one V_MFMA_SCALE_F32_16X16X128_F8F6F4
+// (neutral hardware scales) per 16x16 output tile produces that block's partial
+// sum, which is then promoted into an fp32 register accumulator with the
+// fine-grained scales sa(i, kb) * sb(j/128, kb) (one RHS scale per 128x128
+// block, whose row of ceil(k/128) values serves every K block -- the reply in
+// "[Help] Starter script for nn.Linear for fwd,bwd").  Weight gradient
+// ("DeepGEMM Essentials", Parts 12-13: fp32 output, accumulated in place):
+// sa(i, kb) * sb(j, kb), with the block sums taken on the f16 MFMA
+// (gemm_wgrad_kernel explains why).
 //
 // gfx950 design notes (measured on MI355X):
 //  * The FP8 MFMA sustains ~4.6 PF, but dependent fp32 VALU work issued right
 //    after it serialises with it.  So the promotion of block kb-1's partial
 //    sums is software-pipelined under block kb's MFMAs: each MFMA writes a
 //    fresh partial P[t] that is consumed one K block later, and the issue
-//    order is shaped MFMA / VALU / MFMA / VALU with sched_group_barrier.
+//    order is pinned MFMA by MFMA with sched_barrier.
 //    (The MFMA results are kept in VGPRs: -mllvm --amdgpu-mfma-vgpr-form.)
 //  * A and B K-tiles (128 bytes of K per row) are copied global -> LDS by
 //    global_load_lds_dwordx4 (no VGPR staging), two stages deep.  Each lane
@@ -33,6 +34,7 @@
 //    the two stages cannot hide: the first round of workgroups reads all of B
 //    once, and each weight-gradient tile reads its D, right after block 0's
 //    copies (overlapped with block 0's MFMAs).
+//  * Weight-gradient, decode-sized and UE8M0 variants follow below.
 #include <atomic>
 
 #include "device_common.h"
@@ -125,11 +127,10 @@ __device__ __forceinline__ float load_sa(const void *sa, int64_t sa_ld, int64_t 
   }
 }
 
-// Scales of one K block as the promotion uses them.
+// Scales of one K block as the forward / dgrad promotion uses them.
 struct BlockScales {
   float sa[4];      // per row-subtile (the lane's row)
-  float sb;         // forward/dgrad: uniform over the wave's 64 columns
-  v4f sbj[4];       // wgrad: per column-subtile, 4 consecutive columns
+  float sb;         // uniform over the wave's 64 columns (one 128x128 block of B)
 };
 
 // As load_lds16 with 4 bytes per lane (lane l's dword lands at dst + 4*l).
@@ -178,16 +179,103 @@ __device__ __forceinline__ bool d_prefetch(const GemmArgs &g, int64_t m0, int64_
   return true;
 }
 
-// acc += P * scale for MFMA tile (mi, ni)
-template <bool WGRAD>
-__device__ __forceinline__ void promote(v4f &acc, const v4f &p, const BlockScales &s, int mi, int ni) {
-  if constexpr (!WGRAD) {
-    const float c = s.sa[mi] * s.sb;
+// acc += P * sa(i, kb) * sb(j/128, kb) for an MFMA tile of row-subtile mi
+__device__ __forceinline__ void promote(v4f &acc, const v4f &p, const BlockScales &s, int mi) {
+  const float c = s.sa[mi] * s.sb;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) acc[r] = __builtin_fmaf(p[r], c, acc[r]);
-  } else {
+  for (int r = 0; r < 4; ++r) acc[r] = __builtin_fmaf(p[r], c, acc[r]);
+}
+
+// Tile of workgroup blockIdx.x: block b runs on XCD b % 8, each XCD takes a
+// contiguous range of tile ids, walked in bands of kGroupM m-tiles, so that the
+// tiles resident on one XCD share A and B panels in its L2.  False for the
+// workgroups past the last tile (the grid is a whole number of XCD ranges).
+template <class C>
+__device__ __forceinline__ bool tile_origin(int tiles_m, int tiles_n, int64_t &m0, int64_t &n0) {
+  const int tiles = tiles_m * tiles_n;
+  const int per_xcd = (tiles + kXcds - 1) / kXcds;
+  const int tid = (int)(blockIdx.x % kXcds) * per_xcd + (int)(blockIdx.x / kXcds);
+  if (tid >= tiles) return false;
+  const int band = tid / (kGroupM * tiles_n);
+  const int band_m = min(kGroupM, tiles_m - band * kGroupM);
+  const int in_band = tid - band * kGroupM * tiles_n;
+  m0 = (int64_t)(band * kGroupM + in_band % band_m) * C::kBM;
+  n0 = (int64_t)(in_band / band_m) * C::kBN;
+  return true;
+}
+
+// Direct-to-LDS copies of the A and B tiles of one K block (128 bytes of K per
+// row).  Offsets are 32-bit from the tile's first row (the host bounds lda, ldb
+// below 2^24).  Each 1 KB wave instruction fills 64 consecutive 16-byte slots:
+// slot s holds row s/8, physical chunk s%8, i.e. logical chunk (s%8) ^
+// swz_key(row).  Wave wv issues tile instructions wv, wv + kWaves, ...; rows past
+// the matrix edge read its last row (their results are never stored).  The scale
+// rows (4 bytes per lane) are spread over the first waves: sa's kBM rows, then
+// sb's kBN columns (or its one block scale).
+template <class C>
+struct TileCopy {
+  uint32_t a_off[C::kALoads], b_off[C::kBLoads];
+  bool sa_loader, sb_loader;
+  uint32_t scale_off;   // row of sa (or column of sb) this lane copies, times 4
+
+  __device__ __forceinline__ TileCopy(const GemmArgs &g, int64_t m0, int64_t n0, int wv, int lane) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) acc[r] = __builtin_fmaf(p[r], s.sa[mi] * s.sbj[ni][r], acc[r]);
+    for (int i = 0; i < C::kALoads; ++i) {
+      const int s = 64 * (i * C::kWaves + wv) + lane, row = s >> 3, chunk = (s & 7) ^ swz_key(row);
+      a_off[i] = (uint32_t)(min((int64_t)row, g.m - 1 - m0) * g.lda) + (uint32_t)(chunk * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < C::kBLoads; ++i) {
+      const int s = 64 * (i * C::kWaves + wv) + lane, row = s >> 3, chunk = (s & 7) ^ swz_key(row);
+      b_off[i] = (uint32_t)(min((int64_t)row, g.n - 1 - n0) * g.ldb) + (uint32_t)(chunk * 16);
+    }
+    static_assert(C::kSaLoads + C::kSbLoads <= C::kWaves, "one scale load per wave at most");
+    sa_loader = wv < C::kSaLoads;
+    sb_loader = wv >= C::kSaLoads && wv < C::kSaLoads + C::kSbLoads;
+    scale_off = sa_loader ? 4u * (uint32_t)min((int64_t)(64 * wv + lane), g.m - 1 - m0)
+                          : 4u * (uint32_t)min((int64_t)(64 * (wv - C::kSaLoads) + lane), g.n - 1 - n0);
+  }
+  // tiles of the K block whose first bytes are ga (row m0 of A) and gb (row n0 of B)
+  __device__ __forceinline__ void tiles(const uint8_t *ga, const uint8_t *gb, uint8_t *st, int wv) const {
+#pragma unroll
+    for (int i = 0; i < C::kALoads; ++i) load_lds16(ga, a_off[i], st + 1024 * (i * C::kWaves + wv));
+#pragma unroll
+    for (int i = 0; i < C::kBLoads; ++i) load_lds16(gb, b_off[i], st + C::kABytes + 1024 * (i * C::kWaves + wv));
+  }
+  // the scale dwords of the stage: sa_row = &sa(m0, kb) (MN-major), sb_row = &sb(n0, kb)
+  // (MN-major, one per column) or the block scale itself (block_sb: every lane copies it)
+  __device__ __forceinline__ void scales(const void *sa_row, const void *sb_row, bool block_sb, uint8_t *st,
+                                         int wv) const {
+    if (sa_loader)
+      load_lds4(sa_row, scale_off, st + C::kSaOff + 256 * wv);
+    else if (sb_loader)
+      load_lds4(sb_row, block_sb ? 0u : scale_off, st + C::kSbOff + 256 * (wv - C::kSaLoads));
+  }
+};
+
+// Weight-gradient epilogue: D += acc in fp32 for the wave's 64x64 block, a lane
+// holding row i, columns j..j+3 of each 16x16 tile (16-byte read-modify-write).
+__device__ __forceinline__ void wgrad_store(const GemmArgs &g, const v4f (&acc)[16], int64_t m0, int64_t n0,
+                                            int wm, int wn, int lane) {
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi) {
+    const int64_t i = m0 + wm + 16 * mi + (lane & 15);
+    if (i >= g.m) continue;
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) {
+      const int64_t j = n0 + wn + 16 * ni + 4 * (lane >> 4);
+      if (j >= g.n) continue;
+      const v4f a = acc[4 * mi + ni];
+      float *dp = reinterpret_cast<float *>(g.D) + i * g.ldd + j;
+      if (j + 4 <= g.n) {
+        const v4f d = *reinterpret_cast<const v4f *>(dp);
+        *reinterpret_cast<v4f *>(dp) = d + a;
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (j + r < g.n) dp[r] += a[r];
+      }
+    }
   }
 }
 
@@ -252,27 +340,15 @@ __device__ __forceinline__ void fused_cast_epilogue(const GemmArgs &g, const v4f
   }
 }
 
-template <class C, int SA_FMT, bool WGRAD, bool GROUPED, int CASTF>
+template <class C, int SA_FMT, bool GROUPED, int CASTF>
 __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_kernel(GemmArgs g, int tiles_m, int tiles_n) {
-  // the stages, then a 1 KB slot that receives the prefetch copies (B, or a
-  // weight-gradient tile's D)
+  // the stages, then a 1 KB slot that receives the B prefetch copies
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::kStages * C::kStageBytes + 1024];
   const int t = threadIdx.x, lane = t & 63;
   const int wv = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wm = (wv / C::WAVES_N_) * 64, wn = (wv % C::WAVES_N_) * 64;
-
-  // XCD-aware tile order: block b runs on XCD b % 8; each XCD takes a contiguous
-  // range of tile ids, walked in bands of kGroupM m-tiles.
-  const int tiles = tiles_m * tiles_n;
-  const int per_xcd = (tiles + kXcds - 1) / kXcds;
-  const int tid = (int)(blockIdx.x % kXcds) * per_xcd + (int)(blockIdx.x / kXcds);
-  if (tid >= tiles) return;
-  const int band = tid / (kGroupM * tiles_n);
-  const int band_m = min(kGroupM, tiles_m - band * kGroupM);
-  const int in_band = tid - band * kGroupM * tiles_n;
-  const int tm = band * kGroupM + in_band % band_m;
-  const int tn = in_band / band_m;
-  const int64_t m0 = (int64_t)tm * C::kBM, n0 = (int64_t)tn * C::kBN;
+  int64_t m0, n0;
+  if (!tile_origin<C>(tiles_m, tiles_n, m0, n0)) return;
   const int64_t m = g.m, n = g.n;
   const int KB = (int)(g.k / kBK);
 
@@ -295,47 +371,14 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_kernel(GemmAr
     sbg = g.sb + (int64_t)expert * g.sb_estride;
   }
 
-  // Direct-to-LDS copy of one stage (tiles and scales of one K block).  Offsets
-  // are 32-bit from the tile's first row (the host bounds lda, ldb < 2^24).  Each 1 KB
-  // wave instruction fills 64 consecutive 16-byte slots; slot s holds row s/8,
-  // physical chunk s%8, i.e. logical chunk (s%8) ^ swz_key(row).  Wave wv issues
-  // tile instructions wv, wv + kWaves, ...; the scale rows (4 bytes per lane) are
-  // spread over the first waves.
-  uint32_t a_off[C::kALoads], b_off[C::kBLoads];
-#pragma unroll
-  for (int i = 0; i < C::kALoads; ++i) {
-    const int s = 64 * (i * C::kWaves + wv) + lane, row = s >> 3, chunk = (s & 7) ^ swz_key(row);
-    a_off[i] = (uint32_t)(min((int64_t)row, m - 1 - m0) * g.lda) + (uint32_t)(chunk * 16);
-  }
-#pragma unroll
-  for (int i = 0; i < C::kBLoads; ++i) {
-    const int s = 64 * (i * C::kWaves + wv) + lane, row = s >> 3, chunk = (s & 7) ^ swz_key(row);
-    b_off[i] = (uint32_t)(min((int64_t)row, n - 1 - n0) * g.ldb) + (uint32_t)(chunk * 16);
-  }
-  static_assert(C::kSaLoads + C::kSbLoads <= C::kWaves, "one scale load per wave at most");
-  const bool sa_loader = wv < C::kSaLoads;
-  const bool sb_loader = wv >= C::kSaLoads && wv < C::kSaLoads + C::kSbLoads;
-  // row of sa (or column of sb) this lane copies, relative to the tile's first
-  const uint32_t scale_off = sa_loader ? 4u * (uint32_t)min((int64_t)(64 * wv + lane), m - 1 - m0)
-                                       : 4u * (uint32_t)min((int64_t)(64 * (wv - C::kSaLoads) + lane), n - 1 - n0);
+  // One stage: the A and B tiles of K block kb, A's row scales (MN-major; packed
+  // words hold four K blocks) and B's one block scale of the tile.
+  const TileCopy<C> cp(g, m0, n0, wv, lane);
   auto issue = [&](int kb, uint8_t *st) {
-    const uint8_t *ga = g.A + m0 * g.lda + (int64_t)kb * kBK;
-    const uint8_t *gb = Bg + n0 * g.ldb + (int64_t)kb * kBK;
-#pragma unroll
-    for (int i = 0; i < C::kALoads; ++i) load_lds16(ga, a_off[i], st + 1024 * (i * C::kWaves + wv));
-#pragma unroll
-    for (int i = 0; i < C::kBLoads; ++i) load_lds16(gb, b_off[i], st + C::kABytes + 1024 * (i * C::kWaves + wv));
-    if (sa_loader) {
-      const int64_t col = SA_FMT == kSfPackedUe8m0 ? (kb >> 2) : kb;
-      load_lds4(reinterpret_cast<const uint32_t *>(g.sa) + col * g.sa_ld + m0, scale_off,
-                st + C::kSaOff + 256 * wv);
-    } else if (sb_loader) {
-      if constexpr (WGRAD) {
-        load_lds4(g.sb + (int64_t)kb * g.sb_ld + n0, scale_off, st + C::kSbOff + 256 * (wv - C::kSaLoads));
-      } else {   // forward: the tile's one block scale, the same dword in every lane
-        load_lds4(sbg + (n0 >> 7) * g.sb_ld + kb, 0u, st + C::kSbOff + 256 * (wv - C::kSaLoads));
-      }
-    }
+    cp.tiles(g.A + m0 * g.lda + (int64_t)kb * kBK, Bg + n0 * g.ldb + (int64_t)kb * kBK, st, wv);
+    const int64_t col = SA_FMT == kSfPackedUe8m0 ? (kb >> 2) : kb;
+    cp.scales(reinterpret_cast<const uint32_t *>(g.sa) + col * g.sa_ld + m0, sbg + (n0 >> 7) * g.sb_ld + kb, true,
+              st, wv);
   };
   auto read_scales = [&](int kb, const uint8_t *st, BlockScales &s) {
 #pragma unroll
@@ -347,21 +390,13 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_kernel(GemmAr
         s.sa[mi] = v;
       }
     }
-    if constexpr (!WGRAD) {
-      s.sb = *reinterpret_cast<const float *>(st + C::kSbOff);
-    } else {
-#pragma unroll
-      for (int ni = 0; ni < 4; ++ni)
-        s.sbj[ni] = *reinterpret_cast<const v4f *>(st + C::kSbOff + 4 * (wn + 16 * ni + 4 * (lane >> 4)));
-    }
+    s.sb = *reinterpret_cast<const float *>(st + C::kSbOff);
   };
 
   BlockScales prev;   // scales of the K block whose partial sums are pending
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi) prev.sa[mi] = 0.0f;
   prev.sb = 0.0f;
-#pragma unroll
-  for (int ni = 0; ni < 4; ++ni) prev.sbj[ni] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
 
   v4f acc[16], p[16];
 #pragma unroll
@@ -392,16 +427,11 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_kernel(GemmAr
   // Copies complete in order, so the first wait lets exactly those be in flight
   // and block 0's MFMAs overlap them.  Measured on MI355X in the linear step
   // (20 steps back to back): dgrad 291 -> 273 us (its B, W^T, was written long
-  // before), forward +1%, step -1.4%.  The launcher enables it for forward /
-  // dgrad grids of more than one round only.
+  // before), forward +1%, step -1.4%.  The launcher enables it for grids of more
+  // than one round only.
   issue(0, smem);
-  bool prefetching = !GROUPED && (int)blockIdx.x < g.b_prefetch_wgs;
+  const bool prefetching = !GROUPED && (int)blockIdx.x < g.b_prefetch_wgs;
   if (prefetching) b_prefetch<C>(g, n, wv, lane, smem + C::kStages * C::kStageBytes);
-  // The weight gradient reads D at the end, written a whole step earlier: the
-  // tile's D is pulled into the caches the same way (measured on MI355X in the
-  // linear step: wgrad 359 -> 350 us).
-  if constexpr (WGRAD)
-    if (!prefetching) prefetching = d_prefetch<C>(g, m0, n0, wv, lane, smem + C::kStages * C::kStageBytes);
   for (int kb = 0; kb < KB; ++kb) {
     // wave priority 0 while waiting and issuing copies, 3 once its MFMAs run (below):
     // the SIMD's other wave, if it is in its MFMA phase, is served first
@@ -431,7 +461,7 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_kernel(GemmAr
       else if (q < 5) af[q - 1] = frag(st, wm + 16 * (q - 1) + (lane & 15), lane);
       const int mi = q >> 2, ni = (mi & 1) ? 3 - (q & 3) : (q & 3), i = 4 * mi + ni;
       // promote tile i of block kb-1 (scales `prev`) beside block kb's MFMA
-      promote<WGRAD>(acc[i], p[i], prev, mi, ni);
+      promote(acc[i], p[i], prev, mi);
       p[i] = mfma_k128(bf[ni], af[mi]);
       if (q == 0) __builtin_amdgcn_s_setprio(3);
       __builtin_amdgcn_sched_barrier(0);
@@ -439,7 +469,7 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_kernel(GemmAr
     prev = cur;
   }
 #pragma unroll
-  for (int i = 0; i < 16; ++i) promote<WGRAD>(acc[i], p[i], prev, i >> 2, i & 3);
+  for (int i = 0; i < 16; ++i) promote(acc[i], p[i], prev, i >> 2);
 
   // epilogue: lane holds row i, columns j..j+3 of every 16x16 tile
   if constexpr (CASTF != 0) fused_cast_epilogue<C, CASTF == 2>(g, acc, m0, n0, wm, wn, lane);
@@ -458,27 +488,15 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_kernel(GemmAr
       const int64_t j = n0 + wn + 16 * ni + 4 * (lane >> 4);
       if (j >= n) continue;
       const v4f a = acc[4 * mi + ni];
-      if constexpr (!WGRAD) {
-        uint16_t *dp = reinterpret_cast<uint16_t *>(g.D) + i * g.ldd + j;
-        const uint32_t h0 = bf16_rne(a[0]) | (bf16_rne(a[1]) << 16);
-        const uint32_t h1 = bf16_rne(a[2]) | (bf16_rne(a[3]) << 16);
-        if (j + 4 <= n) {
-          *reinterpret_cast<u32x2 *>(dp) = (u32x2){h0, h1};
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (j + r < n) dp[r] = (uint16_t)bf16_rne(a[r]);
-        }
+      uint16_t *dp = reinterpret_cast<uint16_t *>(g.D) + i * g.ldd + j;
+      const uint32_t h0 = bf16_rne(a[0]) | (bf16_rne(a[1]) << 16);
+      const uint32_t h1 = bf16_rne(a[2]) | (bf16_rne(a[3]) << 16);
+      if (j + 4 <= n) {
+        *reinterpret_cast<u32x2 *>(dp) = (u32x2){h0, h1};
       } else {
-        float *dp = reinterpret_cast<float *>(g.D) + i * g.ldd + j;
-        if (j + 4 <= n) {
-          const v4f d = *reinterpret_cast<const v4f *>(dp);
-          *reinterpret_cast<v4f *>(dp) = d + a;
-        } else {
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (j + r < n) dp[r] += a[r];
-        }
+        for (int r = 0; r < 4; ++r)
+          if (j + r < n) dp[r] = (uint16_t)bf16_rne(a[r]);
       }
     }
   }
@@ -496,9 +514,8 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_kernel(GemmAr
 // scaling then happens inside the MFMA, which accumulates straight into the
 // fp32 accumulator: no promotion.  Each register half holds 16 consecutive
 // K bytes, so the MFMA's runs of 8 products are still 8 consecutive K.  Tiles,
-// copies, waits and fragment order are those of gemm_kernel.  The weight-gradient
-// form ("DeepGEMM Essentials", Parts 12-13: K runs over tokens, fp32 output
-// accumulated in place) differs only in its epilogue.
+// copies, waits and fragment order are those of gemm_kernel.  (The weight
+// gradients with these scales run on gemm_wgrad_kernel, for its precision.)
 __device__ __forceinline__ v8i frag_g32(const uint8_t *tile, int row, int lane) {
   const int c = lane >> 4;
   const u32x4 lo = *reinterpret_cast<const u32x4 *>(tile + swz(row, c));
@@ -517,24 +534,15 @@ __device__ __forceinline__ v8i frag_g32(const uint8_t *tile, int row, int lane) 
 // sb[nb*sb_ld + kb], the same exponent for every column of the tile.
 enum : int { kUeG32Packed = 0, kUeG128Packed = 1, kUeG128Float = 2, kUeBlockFloat = 3 };
 
-template <class C, bool WGRAD, bool GROUPED, int SMODE = kUeG32Packed, int SB_MODE = SMODE>
+template <class C, bool GROUPED, int SMODE = kUeG32Packed, int SB_MODE = SMODE>
 __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_g32_kernel(GemmArgs g, int tiles_m, int tiles_n) {
-  // the stages, then a 1 KB slot that receives the prefetch copies (B, or a
-  // weight-gradient tile's D)
+  // the stages, then a 1 KB slot that receives the B prefetch copies
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::kStages * C::kStageBytes + 1024];
   const int t = threadIdx.x, lane = t & 63;
   const int wv = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wm = (wv / C::WAVES_N_) * 64, wn = (wv % C::WAVES_N_) * 64;
-  const int tiles = tiles_m * tiles_n;
-  const int per_xcd = (tiles + kXcds - 1) / kXcds;
-  const int tid = (int)(blockIdx.x % kXcds) * per_xcd + (int)(blockIdx.x / kXcds);
-  if (tid >= tiles) return;
-  const int band = tid / (kGroupM * tiles_n);
-  const int band_m = min(kGroupM, tiles_m - band * kGroupM);
-  const int in_band = tid - band * kGroupM * tiles_n;
-  const int tm = band * kGroupM + in_band % band_m;
-  const int tn = in_band / band_m;
-  const int64_t m0 = (int64_t)tm * C::kBM, n0 = (int64_t)tn * C::kBN;
+  int64_t m0, n0;
+  if (!tile_origin<C>(tiles_m, tiles_n, m0, n0)) return;
   const int64_t m = g.m, n = g.n;
   const int KB = (int)(g.k / kBK);
 
@@ -555,42 +563,16 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_g32_kernel(Ge
     sbw += (int64_t)expert * g.sb_estride;
   }
 
-  uint32_t a_off[C::kALoads], b_off[C::kBLoads];
-#pragma unroll
-  for (int i = 0; i < C::kALoads; ++i) {
-    const int s = 64 * (i * C::kWaves + wv) + lane, row = s >> 3, chunk = (s & 7) ^ swz_key(row);
-    a_off[i] = (uint32_t)(min((int64_t)row, m - 1 - m0) * g.lda) + (uint32_t)(chunk * 16);
-  }
-#pragma unroll
-  for (int i = 0; i < C::kBLoads; ++i) {
-    const int s = 64 * (i * C::kWaves + wv) + lane, row = s >> 3, chunk = (s & 7) ^ swz_key(row);
-    b_off[i] = (uint32_t)(min((int64_t)row, n - 1 - n0) * g.ldb) + (uint32_t)(chunk * 16);
-  }
-  // scale words of block kb: the tile's rows (A) then its columns (B), 64 per wave
-  static_assert(C::kSaLoads + C::kSbLoads <= C::kWaves, "one scale load per wave at most");
-  const bool sa_loader = wv < C::kSaLoads;
-  const bool sb_loader = wv >= C::kSaLoads && wv < C::kSaLoads + C::kSbLoads;
-  const uint32_t scale_off = sa_loader ? 4u * (uint32_t)min((int64_t)(64 * wv + lane), m - 1 - m0)
-                                       : 4u * (uint32_t)min((int64_t)(64 * (wv - C::kSaLoads) + lane), n - 1 - n0);
+  // one stage: the A and B tiles of K block kb and the scale words of the tile's
+  // rows (A) and columns (B), or B's one block scale
+  const TileCopy<C> cp(g, m0, n0, wv, lane);
   const uint32_t *saw = reinterpret_cast<const uint32_t *>(g.sa);
   auto issue = [&](int kb, uint8_t *st) {
-    const uint8_t *ga = g.A + m0 * g.lda + (int64_t)kb * kBK;
-    const uint8_t *gb = Bg + n0 * g.ldb + (int64_t)kb * kBK;
-#pragma unroll
-    for (int i = 0; i < C::kALoads; ++i) load_lds16(ga, a_off[i], st + 1024 * (i * C::kWaves + wv));
-#pragma unroll
-    for (int i = 0; i < C::kBLoads; ++i) load_lds16(gb, b_off[i], st + C::kABytes + 1024 * (i * C::kWaves + wv));
-    if (sa_loader) {
-      const int64_t col = SMODE == kUeG128Packed ? (kb >> 2) : kb;
-      load_lds4(saw + col * g.sa_ld + m0, scale_off, st + C::kSaOff + 256 * wv);
-    } else if (sb_loader) {
-      if constexpr (SB_MODE == kUeBlockFloat) {   // the tile's one block scale, the same dword in every lane
-        load_lds4(sbw + (n0 >> 7) * g.sb_ld + kb, 0u, st + C::kSbOff + 256 * (wv - C::kSaLoads));
-      } else {
-        const int64_t col = SB_MODE == kUeG128Packed ? (kb >> 2) : kb;
-        load_lds4(sbw + col * g.sb_ld + n0, scale_off, st + C::kSbOff + 256 * (wv - C::kSaLoads));
-      }
-    }
+    cp.tiles(g.A + m0 * g.lda + (int64_t)kb * kBK, Bg + n0 * g.ldb + (int64_t)kb * kBK, st, wv);
+    const int64_t col_a = SMODE == kUeG128Packed ? (kb >> 2) : kb;
+    const int64_t col_b = SB_MODE == kUeG128Packed ? (kb >> 2) : kb;
+    const uint32_t *sb_row = SB_MODE == kUeBlockFloat ? sbw + (n0 >> 7) * g.sb_ld + kb : sbw + col_b * g.sb_ld + n0;
+    cp.scales(saw + col_a * g.sa_ld + m0, sb_row, SB_MODE == kUeBlockFloat, st, wv);
   };
 
   v4f acc[16];
@@ -601,12 +583,9 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_g32_kernel(Ge
   auto shift0 = [&](int mode) { return mode == kUeG32Packed ? 8 * (lane >> 4) : mode == kUeG128Packed ? 0 : 23; };
   const int gsh_a0 = shift0(SMODE), gsh_b0 = shift0(SB_MODE);
   issue(0, smem);
-  // B prefetch of the first round of workgroups, and the weight gradient's D
-  // prefetch of the other tiles, as in gemm_kernel
-  bool prefetching = !GROUPED && (int)blockIdx.x < g.b_prefetch_wgs;
+  // B prefetch of the first round of workgroups, as in gemm_kernel
+  const bool prefetching = !GROUPED && (int)blockIdx.x < g.b_prefetch_wgs;
   if (prefetching) b_prefetch<C>(g, n, wv, lane, smem + C::kStages * C::kStageBytes);
-  if constexpr (WGRAD)
-    if (!prefetching) prefetching = d_prefetch<C>(g, m0, n0, wv, lane, smem + C::kStages * C::kStageBytes);
   for (int kb = 0; kb < KB; ++kb) {
     if (prefetching && kb == 0)   // block 0 has landed; the prefetch copies may be in flight
       asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier\n\ts_setprio 0" ::"n"(kPrefetch) : "memory");
@@ -652,29 +631,207 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_g32_kernel(Ge
       const int64_t j = n0 + wn + 16 * ni + 4 * (lane >> 4);
       if (j >= n) continue;
       const v4f a = acc[4 * mi + ni];
-      if constexpr (!WGRAD) {
-        uint16_t *dp = reinterpret_cast<uint16_t *>(g.D) + i * g.ldd + j;
-        if (j + 4 <= n) {
-          *reinterpret_cast<u32x2 *>(dp) = (u32x2){bf16_rne(a[0]) | (bf16_rne(a[1]) << 16),
-                                                   bf16_rne(a[2]) | (bf16_rne(a[3]) << 16)};
-        } else {
+      uint16_t *dp = reinterpret_cast<uint16_t *>(g.D) + i * g.ldd + j;
+      if (j + 4 <= n) {
+        *reinterpret_cast<u32x2 *>(dp) = (u32x2){bf16_rne(a[0]) | (bf16_rne(a[1]) << 16),
+                                                 bf16_rne(a[2]) | (bf16_rne(a[3]) << 16)};
+      } else {
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (j + r < n) dp[r] = (uint16_t)bf16_rne(a[r]);
-        }
-      } else {   // weight gradient: fp32, added to what D holds
-        float *dp = reinterpret_cast<float *>(g.D) + i * g.ldd + j;
-        if (j + 4 <= n) {
-          const v4f d = *reinterpret_cast<const v4f *>(dp);
-          *reinterpret_cast<v4f *>(dp) = d + a;
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (j + r < n) dp[r] += a[r];
-        }
+        for (int r = 0; r < 4; ++r)
+          if (j + r < n) dp[r] = (uint16_t)bf16_rne(a[r]);
       }
     }
   }
+}
+
+// Weight gradient ("DeepGEMM Essentials", Parts 12-13: K runs over tokens, both
+// operands carry one scale per row and 128-token block -- or, in the UE8M0
+// recipes, a power of two per row and 128- or 32-token group -- and the fp32
+// output is accumulated in place) on the f16 / bf16 MFMA.
+//
+// Why not the FP8 MFMA: it adds each run of 8 consecutive K products after
+// aligning them to the run's largest exponent sum with 13 fraction bits,
+// truncated, which on randn operands leaves a relative Frobenius error of
+// 1.35e-5 (fp32 scales) to 1.5e-5 (UE8M0 scales) in a 4096 x 7168 gradient over
+// 8192 tokens, above the 1e-5 the gradient must meet.  V_MFMA_F32_16X16X32_F16
+// and _BF16 sum a 128-wide K block to within ~1e-8 (measured on MI355X), and
+// every E4M3 value is exact in f16 and in bf16, so this kernel keeps
+// gemm_kernel's FP8 tiles, copies and pipeline and widens the fragments in
+// registers just before the MFMAs (V_CVT_SCALEF32_PK_F16_FP8 / _BF16_FP8: exact
+// for all 256 codes, and for bf16 also after a power-of-two scale).  A lane's 32
+// K bytes of a fragment row are read 16 at a time; 8-byte slice s feeds the
+// block's s-th MFMA, in the same order for both operands, so the four MFMAs of a
+// tile add all 128 products of the block.  With fp32 scales they go into a fresh
+// partial sum P, promoted with sa(i, kb) * sb(j, kb) in the block's last slice,
+// each tile four MFMAs after its last one.
+//
+// Cost, measured on MI355X: a conversion takes ~4 clocks per two values and a
+// VALU instruction overlaps an MFMA only for the first ~2 per MFMA, so with two
+// conversions and two promotion instructions per MFMA the fp32-scale kernel is
+// bound by the VALU: 452-481 us for 4096 x 7168 x 8192, against 305-311 us for
+// the same pipeline on the FP8 MFMA.
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef __bf16 b8 __attribute__((ext_vector_type(8)));
+
+// f16 operand of slice s (0 or 1) of 16 FP8 bytes: bytes 8s..8s+7, in order
+__device__ __forceinline__ h8 slice_f16(const u32x4 &raw, int s) {
+  const uint32_t w0 = raw[2 * s], w1 = raw[2 * s + 1];
+  const u32x4 d = {__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, false)),
+                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, true)),
+                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, false)),
+                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, true))};
+  return __builtin_bit_cast(h8, d);
+}
+
+// bf16 operand of slice s of 16 FP8 bytes, each value times the power of two
+// `scale` (exact: E4M3 has 4 significant bits, bf16 8, and the exponent range of
+// fp32)
+__device__ __forceinline__ b8 slice_bf16(const u32x4 &raw, int s, float scale) {
+  const uint32_t w0 = raw[2 * s], w1 = raw[2 * s + 1];
+  const u32x4 d = {__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, scale, false)),
+                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, scale, true)),
+                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, scale, false)),
+                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, scale, true))};
+  return __builtin_bit_cast(b8, d);
+}
+
+// Scale layouts of the weight-gradient kernel: kWgFp32, one fp32 scale per row and
+// 128-K block (promoted); the UE8M0 layouts of gemm_g32_kernel (kUeG32Packed,
+// kUeG128Packed, kUeG128Float) on both operands, folded into the conversion.
+constexpr int kWgFp32 = -1;
+
+// Weight-gradient kernel.  SMODE == kWgFp32: fragments widened to f16 (scale 1),
+// the block's partial sums promoted with sa(i, kb) * sb(j, kb).  UE8M0 layouts:
+// each fragment widened to bf16 times its row's power of two for the lane's
+// 32-K group (the lane of group G = lane/16 holds K bytes 32G..32G+31 of the
+// block, so with 1x32 groups that is byte G of the block's word), and the MFMAs
+// accumulate straight into the output registers over all of K: no promotion.
+template <class C, int SMODE>
+__global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_wgrad_kernel(GemmArgs g, int tiles_m,
+                                                                               int tiles_n) {
+  static_assert(C::kBM == 128 && C::kBN == 128 && C::kStages == 2, "128x128 tiles, two stages");
+  constexpr bool kUe = SMODE != kWgFp32;
+  // the stages, then a 1 KB slot that receives the D prefetch copies
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::kStages * C::kStageBytes + 1024];
+  const int t = threadIdx.x, lane = t & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wm = (wv / C::WAVES_N_) * 64, wn = (wv % C::WAVES_N_) * 64;
+  int64_t m0, n0;
+  if (!tile_origin<C>(tiles_m, tiles_n, m0, n0)) return;
+  const int KB = (int)(g.k / kBK);
+
+  // one stage: the A and B tiles of K block kb, sa's rows and sb's columns (MN-major;
+  // packed 1x128 words hold four K blocks)
+  const TileCopy<C> cp(g, m0, n0, wv, lane);
+  const uint32_t *saw = reinterpret_cast<const uint32_t *>(g.sa);
+  const uint32_t *sbw = reinterpret_cast<const uint32_t *>(g.sb);
+  auto issue = [&](int kb, uint8_t *st) {
+    cp.tiles(g.A + m0 * g.lda + (int64_t)kb * kBK, g.B + n0 * g.ldb + (int64_t)kb * kBK, st, wv);
+    const int64_t col = SMODE == kUeG128Packed ? (kb >> 2) : kb;
+    cp.scales(saw + col * g.sa_ld + m0, sbw + col * g.sb_ld + n0, false, st, wv);
+  };
+
+  v4f acc[16], p[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+
+  // Two stages, waits and wave priorities as in gemm_kernel.  D is read at the
+  // end, written a whole step earlier: the tile's D is pulled into the caches
+  // behind block 0's copies (d_prefetch).
+  issue(0, smem);
+  const bool prefetching = d_prefetch<C>(g, m0, n0, wv, lane, smem + C::kStages * C::kStageBytes);
+  for (int kb = 0; kb < KB; ++kb) {
+    if (prefetching && kb == 0)   // block 0 has landed; the prefetch copies may be in flight
+      asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier\n\ts_setprio 0" ::"n"(kPrefetch) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier\n\ts_setprio 0" ::: "memory");
+    const uint8_t *st = smem + (kb & 1) * C::kStageBytes;
+    if (kb + 1 < KB) issue(kb + 1, smem + ((kb + 1) & 1) * C::kStageBytes);
+    // scale words of the lane's rows: row-subtile mi of A, column-subtile ni of B
+    uint32_t wa[4], wb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      wa[i] = *reinterpret_cast<const uint32_t *>(st + C::kSaOff + 4 * (wm + 16 * i + (lane & 15)));
+      wb[i] = *reinterpret_cast<const uint32_t *>(st + C::kSbOff + 4 * (wn + 16 * i + (lane & 15)));
+    }
+    float ea[4], eb[4];   // UE8M0: the lane's powers of two for this block
+    v4f sbj[4];           // fp32: column scales of each column-subtile (the lane's 4 columns)
+    if constexpr (kUe) {
+      const int sh = SMODE == kUeG32Packed ? 8 * (lane >> 4) : SMODE == kUeG128Packed ? 8 * (kb & 3) : 23;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        ea[i] = __uint_as_float(((wa[i] >> sh) & 0xFFu) << 23);
+        eb[i] = __uint_as_float(((wb[i] >> sh) & 0xFFu) << 23);
+      }
+    } else {
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni)
+        sbj[ni] = *reinterpret_cast<const v4f *>(st + C::kSbOff + 4 * (wn + 16 * ni + 4 * (lane >> 4)));
+    }
+    // tile at snake position q (row 0 left to right, row 1 right to left, ...)
+    auto tile = [](int q, int &mi, int &ni) {
+      mi = q >> 2;
+      ni = (mi & 1) ? 3 - (q & 3) : (q & 3);
+    };
+    auto promote_tile = [&](int q) {
+      int mi, ni;
+      tile(q, mi, ni);
+      const int i = 4 * mi + ni;
+      const float sa = __uint_as_float(wa[mi]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[i][r] = __builtin_fmaf(p[i][r], sa * sbj[ni][r], acc[i][r]);
+    };
+    u32x4 af[4], bf[4];   // 16 K bytes of each fragment row: slices 2h and 2h + 1
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      if ((s & 1) == 0) {
+        const int c = 2 * (lane >> 4) + (s >> 1);   // the frag() layout's chunk of this half
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          af[i] = *reinterpret_cast<const u32x4 *>(st + swz(wm + 16 * i + (lane & 15), c));
+          bf[i] = *reinterpret_cast<const u32x4 *>(st + C::kABytes + swz(wn + 16 * i + (lane & 15), c));
+        }
+      }
+      if constexpr (kUe) {
+        b8 ah[4], bh[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          ah[i] = slice_bf16(af[i], s & 1, ea[i]);
+          bh[i] = slice_bf16(bf[i], s & 1, eb[i]);
+        }
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          int mi, ni;
+          tile(q, mi, ni);
+          const int i = 4 * mi + ni;
+          acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bh[ni], ah[mi], acc[i], 0, 0, 0);
+          if (s == 0 && q == 0) __builtin_amdgcn_s_setprio(3);
+        }
+      } else {
+        h8 ah[4], bh[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          ah[i] = slice_f16(af[i], s & 1);
+          bh[i] = slice_f16(bf[i], s & 1);
+        }
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          int mi, ni;
+          tile(q, mi, ni);
+          const int i = 4 * mi + ni;
+          const v4f c = s == 0 ? (v4f){0.0f, 0.0f, 0.0f, 0.0f} : p[i];
+          p[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bh[ni], ah[mi], c, 0, 0, 0);
+          if (s == 0 && q == 0) __builtin_amdgcn_s_setprio(3);
+          if (s == 3 && q >= 4) promote_tile(q - 4);
+        }
+      }
+    }
+    if constexpr (!kUe) {
+#pragma unroll
+      for (int q = 12; q < 16; ++q) promote_tile(q);
+    }
+  }
+  wgrad_store(g, acc, m0, n0, wm, wn, lane);
 }
 
 // Skinny (decode-sized) problems, m <= 16*MT: there is too little output to fill
@@ -818,31 +975,31 @@ hipError_t launch_cfg(const GemmArgs &args, hipStream_t st) {
   const int per_xcd = (tiles + kXcds - 1) / kXcds;
   const dim3 grid((unsigned)(per_xcd * kXcds));
   GemmArgs a = args;
-  // B prefetch for forward / dgrad grids of more than one round of tiles (the
-  // wgrad's B is twice as large and shared by fewer XCDs per round: measured
-  // 1-3% slower with it, as is a one-round grid)
+  // B prefetch for forward / dgrad grids of more than one round of tiles (not for
+  // the weight gradient, whose B is twice as large and shared by fewer XCDs per
+  // round: measured 1-3% slower with it on the FP8 MFMA, as is a one-round grid)
   const int64_t first_round = (int64_t)C::kMinBlocks * cu_count();
   a.b_prefetch_wgs = (!a.wgrad && grid.x > first_round) ? (int)first_round : 0;
-#define FGFP8_GEMM(SAF, WG, GR, CF) \
-  hipLaunchKernelGGL((gemm_kernel<C, SAF, WG, GR, CF>), grid, dim3(C::kThreads), 0, st, a, tiles_m, tiles_n)
+#define FGFP8_GEMM(SAF, GR, CF) \
+  hipLaunchKernelGGL((gemm_kernel<C, SAF, GR, CF>), grid, dim3(C::kThreads), 0, st, a, tiles_m, tiles_n)
   const bool packed = a.sa_fmt == kSfPackedUe8m0;
   if (a.wgrad) {
-    FGFP8_GEMM(kSfFp32, true, false, 0);
+    hipLaunchKernelGGL((gemm_wgrad_kernel<C, kWgFp32>), grid, dim3(C::kThreads), 0, st, a, tiles_m, tiles_n);
   } else if (a.m_idx != nullptr || a.q != nullptr) {
     // the grouped layout and the fused output cast work on 128x128 tiles
     if constexpr (C::kBM == 128 && C::kBN == 128) {
       if (a.m_idx != nullptr) {
-        if (packed) FGFP8_GEMM(kSfPackedUe8m0, false, true, 0); else FGFP8_GEMM(kSfFp32, false, true, 0);
+        if (packed) FGFP8_GEMM(kSfPackedUe8m0, true, 0); else FGFP8_GEMM(kSfFp32, true, 0);
       } else if (a.cq_fmt == kSfUe8m0) {
-        if (packed) FGFP8_GEMM(kSfPackedUe8m0, false, false, 2); else FGFP8_GEMM(kSfFp32, false, false, 2);
+        if (packed) FGFP8_GEMM(kSfPackedUe8m0, false, 2); else FGFP8_GEMM(kSfFp32, false, 2);
       } else {
-        if (packed) FGFP8_GEMM(kSfPackedUe8m0, false, false, 1); else FGFP8_GEMM(kSfFp32, false, false, 1);
+        if (packed) FGFP8_GEMM(kSfPackedUe8m0, false, 1); else FGFP8_GEMM(kSfFp32, false, 1);
       }
     } else {
       return hipErrorInvalidValue;
     }
   } else {
-    if (packed) FGFP8_GEMM(kSfPackedUe8m0, false, false, 0); else FGFP8_GEMM(kSfFp32, false, false, 0);
+    if (packed) FGFP8_GEMM(kSfPackedUe8m0, false, 0); else FGFP8_GEMM(kSfFp32, false, 0);
   }
 #undef FGFP8_GEMM
   return hipGetLastError();
@@ -866,31 +1023,32 @@ hipError_t launch_gemm_g32(const GemmArgs &args, hipStream_t st) {
   const int tiles_m = (int)((args.m + C::kBM - 1) / C::kBM), tiles_n = (int)((args.n + C::kBN - 1) / C::kBN);
   const int per_xcd = (tiles_m * tiles_n + kXcds - 1) / kXcds;
   const dim3 grid((unsigned)(per_xcd * kXcds));
-  // B prefetch for grids of more than one round (here the weight gradient too:
-  // measured in the group-32 step, wgrad 298 -> 289 us)
   GemmArgs a = args;
+  // weight gradient: UE8M0 scales folded into the bf16 conversion (no B prefetch,
+  // as for the fp32-scale weight gradient)
+  if (a.wgrad) {
+    if (a.ue_gran == 32)
+      hipLaunchKernelGGL((gemm_wgrad_kernel<C, kUeG32Packed>), grid, dim3(C::kThreads), 0, st, a, tiles_m, tiles_n);
+    else if (a.sa_fmt == kSfPackedUe8m0)
+      hipLaunchKernelGGL((gemm_wgrad_kernel<C, kUeG128Packed>), grid, dim3(C::kThreads), 0, st, a, tiles_m, tiles_n);
+    else
+      hipLaunchKernelGGL((gemm_wgrad_kernel<C, kUeG128Float>), grid, dim3(C::kThreads), 0, st, a, tiles_m, tiles_n);
+    return hipGetLastError();
+  }
+  // B prefetch for grids of more than one round
   const int64_t first_round = (int64_t)C::kMinBlocks * cu_count();
   a.b_prefetch_wgs = grid.x > first_round ? (int)first_round : 0;
-  if (a.wgrad && a.ue_gran == 128)   // UE8M0 1x128 scales on both operands
+  if (a.ue_gran == 128)   // forward / dgrad with UE8M0 1x128 A scales and 128x128 B block scales
     if (a.sa_fmt == kSfPackedUe8m0)
-      hipLaunchKernelGGL((gemm_g32_kernel<C, true, false, kUeG128Packed>), grid, dim3(C::kThreads), 0, st, a, tiles_m,
-                         tiles_n);
+      hipLaunchKernelGGL((gemm_g32_kernel<C, false, kUeG128Packed, kUeBlockFloat>), grid, dim3(C::kThreads), 0, st, a,
+                         tiles_m, tiles_n);
     else
-      hipLaunchKernelGGL((gemm_g32_kernel<C, true, false, kUeG128Float>), grid, dim3(C::kThreads), 0, st, a, tiles_m,
-                         tiles_n);
-  else if (a.wgrad)
-    hipLaunchKernelGGL((gemm_g32_kernel<C, true, false>), grid, dim3(C::kThreads), 0, st, a, tiles_m, tiles_n);
-  else if (a.ue_gran == 128)   // forward / dgrad with UE8M0 1x128 A scales and 128x128 B block scales
-    if (a.sa_fmt == kSfPackedUe8m0)
-      hipLaunchKernelGGL((gemm_g32_kernel<C, false, false, kUeG128Packed, kUeBlockFloat>), grid, dim3(C::kThreads), 0,
-                         st, a, tiles_m, tiles_n);
-    else
-      hipLaunchKernelGGL((gemm_g32_kernel<C, false, false, kUeG128Float, kUeBlockFloat>), grid, dim3(C::kThreads), 0,
-                         st, a, tiles_m, tiles_n);
+      hipLaunchKernelGGL((gemm_g32_kernel<C, false, kUeG128Float, kUeBlockFloat>), grid, dim3(C::kThreads), 0, st, a,
+                         tiles_m, tiles_n);
   else if (a.m_idx != nullptr)
-    hipLaunchKernelGGL((gemm_g32_kernel<C, false, true>), grid, dim3(C::kThreads), 0, st, a, tiles_m, tiles_n);
+    hipLaunchKernelGGL((gemm_g32_kernel<C, true>), grid, dim3(C::kThreads), 0, st, a, tiles_m, tiles_n);
   else
-    hipLaunchKernelGGL((gemm_g32_kernel<C, false, false>), grid, dim3(C::kThreads), 0, st, a, tiles_m, tiles_n);
+    hipLaunchKernelGGL((gemm_g32_kernel<C, false>), grid, dim3(C::kThreads), 0, st, a, tiles_m, tiles_n);
   return hipGetLastError();
 }
 

@@ -1,4 +1,4 @@
-// launch.h -- internal interface between the C ABI (abi.cpp) and the kernel
+// launch.h -- internal interface between the C ABI (abi.hip) and the kernel
 // files of libfgfp8.  Arguments arrive here already validated.
 #pragma once
 
@@ -36,9 +36,11 @@ struct CastBlockArgs {
   int64_t sfT_ld;
 };
 
-// Dual-orientation per-token cast (bf16 input, group 128, fp32 or UE8M0 scales).
+// Dual-orientation per-token cast (bf16 or fp32 input, group 32 or 128, fp32,
+// UE8M0 or packed-UE8M0 scales).
 struct CastDualArgs {
   const void *x;
+  int x_dtype;
   int64_t rows, cols, x_ld;
   int gran_k, sf_fmt;
   uint8_t *q;

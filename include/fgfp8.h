@@ -120,7 +120,7 @@ int cast_per_block(const void *x, int x_dtype, int64_t rows, int64_t cols, int64
                    void *stream);
 
 /*
- * cast_per_token_dual -- both per-token casts of one bf16 matrix from a single
+ * cast_per_token_dual -- both per-token casts of one bf16 or fp32 matrix from a single
  * read: the row-wise cast of x [rows, cols] (1 x gran_k groups along cols) and
  * the row-wise cast of its transpose x^T [cols, rows] (1 x gran_k groups along
  * rows).  Each output is bit-identical to the corresponding cast_per_token
@@ -133,8 +133,9 @@ int cast_per_block(const void *x, int x_dtype, int64_t rows, int64_t cols, int64
  * cast in Triton".  With gran_k = 32 and packed scales it also casts a weight
  * W for the group-32 recipe: q feeds the forward GEMM, qT the dgrad GEMM.
  *
- * x        bf16 [rows, cols] row-major, x_ld >= cols and a multiple of 8
- *          elements; 16-byte aligned.  x_dtype must be FGFP8_IN_BF16.
+ * x        bf16 (x_dtype FGFP8_IN_BF16) or fp32 (FGFP8_IN_FP32) [rows, cols]
+ *          row-major, x_ld >= cols, rows of a multiple of 16 bytes (x_ld a
+ *          multiple of 8 bf16 or 4 fp32 elements); 16-byte aligned.
  * gran_k   32 or 128.
  * sf_fmt   FGFP8_SF_FP32, FGFP8_SF_UE8M0 or FGFP8_SF_PACKED_UE8M0.
  * q, sf    as cast_per_token on x: q [rows, cols] (8-byte aligned, q_ld >= cols,

@@ -96,9 +96,19 @@ def mfma_truncation_bound(qa, sa, qb, sb, sb_block=True, idx=None, group=128):
     return out
 
 
+# Literal "2 bf16 ulps" ceiling.  The FP8 MFMA's truncated run sums and the fp32
+# accumulation leave an error of the order of 1e-5 of sum|terms|, which exceeds 2
+# ulps of |ref| only where the terms nearly cancel (|ref| below ~1e-3 of
+# sum|terms|).  Measured on MI355X: 0.09-0.13% of the outputs of every GEMM
+# configuration with more than a few thousand outputs (the record is
+# tests/precision_record.md); asserted: at most 2 + 0.25% of the outputs.
+LITERAL_2ULP_MAX_FRAC = 0.0025
+
+
 def check_bf16_gemm(got_bits, ref, absum, trunc, kblocks, what):
     """Per element |g - ref| <= 2 ulp_bf16(ref) + (KB + 20) 2^-24 sum|terms| + MFMA truncation
-    bound; Frobenius ||g - bf16(ref)|| / ||bf16(ref)|| <= 1e-3."""
+    bound; Frobenius ||g - bf16(ref)|| / ||bf16(ref)|| <= 1e-3; and the count of elements beyond
+    2 ulps of ref itself at most 2 + LITERAL_2ULP_MAX_FRAC of the outputs."""
     got = oracle.bf16_bits_to_f32(got_bits).astype(np.float64)
     err = np.abs(got - ref)
     bound = 2 * bf16_ulp(ref) + (kblocks + 20) * 2.0 ** -24 * absum + trunc
@@ -107,7 +117,42 @@ def check_bf16_gemm(got_bits, ref, absum, trunc, kblocks, what):
     rb = oracle.bf16_bits_to_f32(oracle.round_bf16(ref)).astype(np.float64)
     den = np.linalg.norm(rb)
     frob = np.linalg.norm(got - rb) / (den if den > 0 else 1.0)
-    assert frob <= 1e-3, f"{what}: normalised Frobenius {frob}"
     literal = int((err > 2 * bf16_ulp(ref)).sum())
     print(f"[gemm-parity] {what}: frobenius {frob:.3e}, literal-2ulp excess {literal}/{err.size}", flush=True)
+    assert frob <= 1e-3, f"{what}: normalised Frobenius {frob}"
+    assert literal <= 2 + LITERAL_2ULP_MAX_FRAC * err.size, f"{what}: {literal} of {err.size} beyond 2 ulps"
     return frob, literal
+
+
+# The weight gradient's gate: relative Frobenius error <= 1e-5 against the fp64
+# reference.  Its block sums come from the f16 / bf16 MFMA, which adds products
+# to within fp32 rounding, so the per-element bound is the fp32 accumulation term
+# alone: one rounding per promoted block (fp32 scales) or per MFMA of 32 tokens
+# (UE8M0 scales, accumulated in the MFMA), plus 20 for the final adds.
+WGRAD_REL_MAX = 1e-5
+
+
+def check_wgrad(got, ref, absum, roundings, what, rel_max=WGRAD_REL_MAX):
+    """|g - ref| <= (roundings + 20) 2^-24 (sum|terms| + |D_in|) per element, and
+    ||g - ref|| / ||ref|| <= rel_max."""
+    g = np.asarray(got, dtype=np.float64)
+    err = np.abs(g - ref)
+    bound = (roundings + 20) * 2.0 ** -24 * absum
+    worst = float((err / np.where(bound > 0, bound, 1.0)).max())
+    rel = np.linalg.norm(g - ref) / np.linalg.norm(ref)
+    print(f"[wgrad-parity] {what}: relative Frobenius {rel:.3e}, max|err|/max|ref| {err.max() / np.abs(ref).max():.3e}, "
+          f"worst err/bound {worst:.3f}", flush=True)
+    assert (err <= bound).all(), f"{what}: {(err > bound).sum()} elements out of tolerance"
+    assert rel <= rel_max, f"{what}: relative Frobenius error {rel:.3e} above {rel_max:.0e}"
+    return rel
+
+
+def sample_idx(m, n, count, seed):
+    """``count`` random (i, j) outputs plus the corners of the first and last tiles."""
+    rng = np.random.default_rng(seed)
+    ii = rng.integers(0, m, count)
+    jj = rng.integers(0, n, count)
+    edge_i = np.array([0, m - 1, min(127, m - 1), min(128, m - 1)])
+    edge_j = np.array([0, n - 1, min(127, n - 1), min(128, n - 1)])
+    ei, ej = np.meshgrid(edge_i, edge_j)
+    return np.concatenate([ii, ei.ravel()]), np.concatenate([jj, ej.ravel()])

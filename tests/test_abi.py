@@ -99,7 +99,8 @@ def dual(lib, **kw):
 
 
 @pytest.mark.parametrize("kw", [
-    dict(dt=1), dict(fmt=3), dict(gran=64), dict(gran=0), dict(fmt=2, gran=32, sfr=2, sfg=1),
+    dict(dt=2), dict(dt=-1), dict(dt=1, xld=386), dict(fmt=3), dict(gran=64), dict(gran=0),
+    dict(fmt=2, gran=32, sfr=2, sfg=1),
     dict(fmt=2, gran=32, sfTr=1, sfTg=1), dict(gran=32, sfr=11, sfg=1), dict(rows=-1), dict(x=None), dict(q=None), dict(sf=None), dict(qT=None),
     dict(sfT=None), dict(xld=380), dict(xld=388), dict(x=ctypes.c_void_p(0x10008)), dict(qld=380),
     dict(q=ctypes.c_void_p(0x20004)), dict(qTld=255), dict(qTld=264), dict(qT=ctypes.c_void_p(0x20008)),

@@ -64,10 +64,23 @@ def test_per_token_matrix(gpu, shape, dtype, gran, fmt):
     _check_tok(x, gran, fmt, mn_major=True)
 
 
-@pytest.mark.parametrize("gran,fmt", [(128, 0), (32, 0), (32, 2), (128, 1)])
-def test_per_token_16384x4096(gpu, gran, fmt):
-    x = _cast_input((16384, 4096), torch.bfloat16)
-    _check_tok(x, gran, fmt, mn_major=(fmt != 2))
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+@pytest.mark.parametrize("gran", [32, 128])
+@pytest.mark.parametrize("fmt", FMTS, ids=["fp32", "ue8m0", "packed"])
+def test_per_token_16384x4096(gpu, dtype, gran, fmt):
+    x = _cast_input((16384, 4096), dtype)
+    _check_tok(x, gran, fmt, mn_major=True)
+    _check_tok(x, gran, fmt, mn_major=False)
+
+
+@pytest.mark.parametrize("rows", [2049, 16383])
+@pytest.mark.parametrize("gran,fmt", [(128, 0), (32, 0), (32, 2), (128, 2), (32, 1)])
+def test_per_token_row_quads_partial(gpu, rows, gran, fmt):
+    """MN-major scales with aligned columns and at least 8192 tasks take the row-quad
+    order; rows % 4 != 0 leaves a last quad of 1 or 3 rows, whose scale store is
+    element-wise."""
+    x = _cast_input((rows, 4096), torch.bfloat16)
+    _check_tok(x, gran, fmt, mn_major=True)
 
 
 @pytest.mark.parametrize("tokens", [1, 64, 512, 4096])

@@ -1,4 +1,4 @@
-"""GPU parity of the dual-orientation per-token cast: one read of bf16 x gives
+"""GPU parity of the dual-orientation per-token cast: one read of bf16 or fp32 x gives
 q/sf bit-identical to the oracle's per-token cast of x and qT/sfT bit-identical
 to its per-token cast of x^T (1x128 or 1x32 groups, fp32 / UE8M0 / packed UE8M0
 scales; "DeepGEMM Essentials", Part 3, the wgrad operands of "[Help] Starter
@@ -31,7 +31,7 @@ def _scale_view(rows, groups, mn_major, pad, packed=False):
 def _run_dual(x_cpu, fmt, mn_major=True, gran=128):
     rows, cols = x_cpu.shape
     x_ld = -(-cols // 8) * 8          # the kernel reads 16-byte chunks of each row
-    xbuf = torch.zeros((rows, x_ld), dtype=torch.bfloat16, device="cuda")
+    xbuf = torch.zeros((rows, x_ld), dtype=x_cpu.dtype, device="cuda")
     xbuf[:, :cols] = x_cpu.cuda()
     x = xbuf[:, :cols]
     q_ld = -(-(cols + 8) // 8) * 8
@@ -44,7 +44,7 @@ def _run_dual(x_cpu, fmt, mn_major=True, gran=128):
         G, GT = -(-G // 4), -(-GT // 4)   # words of four groups
     sf, sbuf = _scale_view(rows, G, mn_major, 4, packed)
     sfT, sTbuf = _scale_view(cols, GT, mn_major, 4, packed)
-    say("cast_per_token_dual", (rows, cols), "gran", gran, "fmt", fmt, "mn", mn_major)
+    say("cast_per_token_dual", (rows, cols), x_cpu.dtype, "gran", gran, "fmt", fmt, "mn", mn_major)
     fg.cast_per_token_dual(x, q, sf, qT, sfT, fmt, gran)
     torch.cuda.synchronize()
     got = (q.cpu().numpy(), sf.contiguous().view(torch.int32).cpu().numpy().view(np.uint32),
@@ -88,6 +88,30 @@ def test_dual_group32(gpu, shape, fmt):
 def test_dual_group128_packed(gpu, shape):
     # one packed word spans four 128-column tiles: each tile stores its own byte
     _check(si.cast_workload(*shape, seed=si.SEED_B), oracle.SF_PACKED_UE8M0, mn_major=True, gran=128)
+
+
+# fp32 input ("deep-gemm: fused per-token FP8 cast in Triton" tests bf16 and fp32
+# inputs): every group size and scale format, ragged and single-row shapes, the
+# fp32 extremes of the cast workloads (an all-zero group and a x1e4 group)
+@pytest.mark.parametrize("shape", [(1, 512), (7, 4096), (129, 7168), (64, 1000), (129, 257), (5, 3), (300, 1000),
+                                   (3000, 4096)])
+@pytest.mark.parametrize("gran", [32, 128])
+@pytest.mark.parametrize("fmt", [oracle.SF_FP32, oracle.SF_UE8M0, oracle.SF_PACKED_UE8M0],
+                         ids=["fp32", "ue8m0", "packed"])
+def test_dual_fp32_input(gpu, shape, gran, fmt):
+    _check(si.cast_workload(*shape, seed=si.SEED_A, dtype=torch.float32), fmt, mn_major=True, gran=gran)
+
+
+def test_dual_fp32_input_extremes_row_major(gpu):
+    # fp32 values beyond the bf16 grid: huge, tiny and subnormal magnitudes, row-major scales
+    x = si.randn((256, 384), 5, 1.0, torch.float32)
+    x[0, :128] *= 1e36
+    x[1, 128:256] *= 1e-36
+    x[:, 300] = 1e-42
+    x[200:, 7] = -3.4e38
+    for gran in (32, 128):
+        for fmt in (oracle.SF_FP32, oracle.SF_UE8M0, oracle.SF_PACKED_UE8M0):
+            _check(x, fmt, mn_major=False, gran=gran)
 
 
 @pytest.mark.parametrize("shape", [(300, 200), (1000, 64)])
