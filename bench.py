@@ -31,7 +31,14 @@ sys.path.insert(0, ROOT)
 
 METRIC = "FP8 block-scaled GEMM TFLOPS (% FP8 MFMA peak); cast GB/s (% HBM peak)"
 PEAK_FP8_TFLOPS = 5000.0      # MI355X dense FP8 MFMA
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA (the weight gradient's instruction)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+
+def mfma_peak(op):
+    """Dense peak of the MFMA an op runs on: the weight gradients take their block sums on
+    the bf16 MFMA (FP8 operands widened exactly in registers), the other GEMMs on FP8."""
+    return ("bf16", PEAK_BF16_TFLOPS) if "wgrad" in op else ("fp8", PEAK_FP8_TFLOPS)
 
 
 def parse():
@@ -173,10 +180,15 @@ def timed_ops(torch, ops, steps, warmup):
     return total_ms, per
 
 
-def rate(unit, amount, ms):
+def rate(unit, amount, ms, op=""):
     if unit == "TFLOPS":
         v = amount / (ms * 1e-3) / 1e12
-        return {"ms": ms, "tflops": v, "frac_fp8_peak": v / PEAK_FP8_TFLOPS}
+        r = {"ms": ms, "tflops": v, "frac_fp8_peak": v / PEAK_FP8_TFLOPS}
+        kind, peak = mfma_peak(op)
+        if kind != "fp8":
+            r["mfma"] = kind
+            r[f"frac_{kind}_peak"] = v / peak
+        return r
     v = amount / (ms * 1e-3) / 1e9
     return {"ms": ms, "gbs": v, "frac_hbm_peak": v / PEAK_HBM_GBS}
 
@@ -224,13 +236,13 @@ def _time_graph(torch, fn, reps=20):
     return a.elapsed_time(b) / reps
 
 
-def _measure(torch, unit, amount, fn, reps=20):
+def _measure(torch, unit, amount, fn, reps=20, op=""):
     """Rate from the per-launch time of `reps` graph-captured launches (no host gaps:
     a small kernel's eager time is mostly launch overhead), plus the eager median,
     p10 and p90 of `reps` event-timed launches."""
     q = _time(torch, fn, reps)
     g = _time_graph(torch, fn, reps)
-    r = rate(unit, amount, g)
+    r = rate(unit, amount, g, op)
     r["eager_ms"], r["eager_p10_ms"], r["eager_p90_ms"] = q
     return r
 
@@ -351,7 +363,8 @@ def extra_kernels(fg, torch, si):
     D = torch.zeros((O, I), dtype=torch.float32, device="cuda")
     torch.cuda.synchronize()
     out[f"wgrad_ue8m0_g32_{O}x{I}x{T}"] = _measure(torch, "TFLOPS", 2.0 * O * I * T,
-                                                   lambda: fg.wgrad_gemm_fp8_nt_fp32_ue8m0_g32(A, wa, B, wb, D))
+                                                   lambda: fg.wgrad_gemm_fp8_nt_fp32_ue8m0_g32(A, wa, B, wb, D),
+                                                   op="wgrad")
     del dy, x, A, B, wa, wb, D
     # m-grouped contiguous GEMM: the 8-expert token mix of the grouped-GEMM exercise
     # (hidden 2048), as given and with 32x the tokens per expert
@@ -454,9 +467,32 @@ def cpu_baseline(si, target_s=20.0):
     T = int(min(si.LINEAR["tokens"], max(128, 128 * round(target_s / cal))))
     dt = step(T)
     flops = 3 * 2.0 * T * I * O
-    return {"value": flops / dt / 1e12, "unit": "TFLOPS", "cores": oracle.max_threads(), "kind": "oracle",
+    # the casts alone, one thread and all threads: x [1024, 7168] per token (g128 fp32 scales)
+    x = si.host_array(si.randn((1024, I), si.SEED_A))
+    cast_bytes = x.size * 3 + x.shape[0] * (I // 128) * 4
+    cast_rate = {}
+    for n in (1, threads):
+        oracle.set_threads(n)
+        t0 = time.perf_counter()
+        oracle.cast_per_token(x, 128, oracle.SF_FP32)
+        cast_rate[f"{n}_threads_gbs"] = cast_bytes / (time.perf_counter() - t0) / 1e9
+    oracle.set_threads(threads)
+    return {"value": flops / dt / 1e12, "unit": "TFLOPS", "cores": threads, "kind": "oracle",
+            "cpu_model": _cpu_model(),
             "sample": f"one full linear step (per-token and block casts, forward, dgrad, wgrad; fp64 exact "
-                      f"block sums) at {T} of the 8192 tokens, in=7168, out=4096: {dt:.1f} s"}
+                      f"block sums) at {T} of the 8192 tokens, in=7168, out=4096: {dt:.1f} s",
+            "cast_per_token_1024x7168_g128": cast_rate}
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def _source_digest(files):
@@ -508,9 +544,10 @@ def main():
     ms_step = total_ms / args.steps
     work = lin.work()
     flops_step = sum(work[name][1] for name, _ in ops if work[name][0] == "TFLOPS")
-    kernels = {name: rate(*work[name], per[name]) for name in per}
+    kernels = {name: rate(*work[name], per[name], name) for name in per}
     dom = max((n for n in per if n.startswith("gemm")), key=lambda n: per[n])
     dom_tflops = work[dom][1] / (per[dom] * 1e-3) / 1e12
+    dom_kind, dom_peak = mfma_peak(dom)
     result = {
         "metric": METRIC,
         "value": flops_step / (ms_step * 1e-3) / 1e12,
@@ -522,14 +559,15 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8_e4m3",
+        "dtype": "fp8_e4m3 operands; fp8 MFMA (forward, dgrad), bf16 MFMA (wgrad); fp32 accumulate",
         "data": "synthetic",
         "config": {"workload": "fp8_linear_step tokens=8192 in=7168 out=4096 "
                                "(dual-orientation casts of x and dY, block cast of W, fwd + dgrad + wgrad GEMMs)",
                    "tokens": cfg["tokens"], "d_in": cfg["d_in"], "d_out": cfg["d_out"],
                    "gran_k": 128, "scales": "fp32", "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma", "kernel": dom, "achieved": dom_tflops, "peak": PEAK_FP8_TFLOPS,
-                     "unit": "TFLOP/s", "frac": dom_tflops / PEAK_FP8_TFLOPS, "traffic": measured_traffic(dom),
+        "roofline": {"bound": "mfma", "kernel": dom, "mfma": dom_kind, "achieved": dom_tflops, "peak": dom_peak,
+                     "unit": "TFLOP/s", "frac": dom_tflops / dom_peak, "frac_fp8_peak": dom_tflops / PEAK_FP8_TFLOPS,
+                     "traffic": measured_traffic(dom),
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                      "algorithmic_flop_per_launch": work[dom][1]},
         "kernels": kernels,
@@ -544,13 +582,13 @@ def main():
         u_ms /= 10
         result["extra"]["linear_step_ue8m0_scales"] = {
             "ms_per_step": u_ms, "tflops": flops_step / (u_ms * 1e-3) / 1e12,
-            "kernels": {name: rate(*work[name], u_per[name]) for name in u_per}}
+            "kernels": {name: rate(*work[name], u_per[name], name) for name in u_per}}
         g32 = lin.g32_ops()
         g_ms, g_per = timed_ops(torch, g32, 10, 2)
         g_ms /= 10
         result["extra"]["linear_step_ue8m0_g32"] = {
             "ms_per_step": g_ms, "tflops": flops_step / (g_ms * 1e-3) / 1e12,
-            "kernels": {name: rate(*work[name], g_per[name]) for name in g_per}}
+            "kernels": {name: rate(*work[name], g_per[name], name) for name in g_per}}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(si)
     print(json.dumps(result), flush=True)
