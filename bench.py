@@ -332,6 +332,17 @@ def extra_kernels(fg, torch, si):
         r["gbs"] = nbytes / (r["ms"] * 1e-3) / 1e9
         r["frac_hbm_peak"] = r["gbs"] / PEAK_HBM_GBS
         out[f"gemm_{m}x{n}x{k}"] = r
+        if m <= 64:
+            # the stream-K decode GEMM (K split evenly over the CUs) on the same operands
+            ws = torch.empty((fg.gemm_fp8_nt_bf16_splitk_workspace(m, n, k) // 4,), dtype=torch.float32,
+                             device="cuda")
+            r = _measure(torch, "TFLOPS", 2.0 * m * n * k,
+                         lambda: fg.gemm_fp8_nt_bf16_splitk(A, sa, Bs[next(it) % len(Bs)], sb, D, ws))
+            r["gbs"] = nbytes / (r["ms"] * 1e-3) / 1e9
+            r["frac_hbm_peak"] = r["gbs"] / PEAK_HBM_GBS
+            r["workspace_bytes"] = ws.numel() * 4
+            out[f"gemm_splitk_{m}x{n}x{k}"] = r
+            del ws
         del A, sa, B, sb, D, Bs
     # UE8M0 group-32 recipe (both operands scaled per row and 32-wide K group, applied by the
     # scaled MFMA: no promotion) at the prefill and linear-forward shapes

@@ -35,6 +35,7 @@
 //    once, and each weight-gradient tile reads its D, right after block 0's
 //    copies (overlapped with block 0's MFMAs).
 //  * Weight-gradient, decode-sized and UE8M0 variants follow below.
+#include <algorithm>
 #include <atomic>
 
 #include "device_common.h"
@@ -950,6 +951,194 @@ __global__ __launch_bounds__(64 * W) void gemm_skinny_kernel(GemmArgs g, int til
   }
 }
 
+// Round 4 fp32 values to bf16 (nearest, ties to even) and store them at dp (8-byte
+// aligned), only the first `left` when fewer than 4 columns remain.
+__device__ __forceinline__ void store_bf16x4(uint16_t *dp, const v4f &v, int64_t left) {
+  if (left >= 4) {
+    *reinterpret_cast<u32x2 *>(dp) =
+        (u32x2){bf16_rne(v[0]) | (bf16_rne(v[1]) << 16), bf16_rne(v[2]) | (bf16_rne(v[3]) << 16)};
+  } else {
+    for (int r = 0; r < left; ++r) dp[r] = (uint16_t)bf16_rne(v[r]);
+  }
+}
+
+// Wait until at most n (0 <= n < 32) vector memory operations of this wave are
+// outstanding, then meet the other waves at the barrier.  The count must be an
+// immediate: with n known at compile time (an unrolled loop) the chain folds to one
+// instruction pair.
+template <int N = 0>
+__device__ __forceinline__ void vm_wait_barrier(int n) {
+  if constexpr (N < 32) {
+    if (n == N) {
+      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+      return;
+    }
+    vm_wait_barrier<N + 1>(n);
+  } else {
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  }
+}
+
+// Stream-K decode GEMM (m <= 16*MT <= 64), bf16 output.  The K blocks of all
+// 128-column tiles form one list of units (tile-major, a tile's KB = k/128 blocks
+// in order); workgroup w takes units [w*UPW, w*UPW + UPW), so the work splits into
+// equal shares whatever the tile count, and a share may end inside one tile and
+// start the next.  A workgroup of 8 waves issues every copy of its share at once:
+// A's rows of each unit into LDS (the swizzled layout and direct-to-LDS copies of
+// gemm_kernel, one 1 KB copy per wave per unit), each wave's 16 columns of B
+// straight into registers; then it takes the units in order as they land, one FP8
+// MFMA per 16-row subtile and the fp32 promotion by sa(i, kb) * sb(tile, kb).
+//
+// A tile that one workgroup covers whole is rounded and stored directly.  A tile
+// shared by consecutive workgroups gets each sharer's fp32 partial sum in the
+// workspace (slot 2w for the tile a share starts in, 2w+1 for the one it ends in;
+// a slot holds the 16*MT x 128 fp32 in the order the waves hold them, [wave][row
+// subtile][lane][4], so each store is 1 KB contiguous), and streamk_fixup_kernel
+// adds them in workgroup order next.
+template <int MT, int UPW, int SA_FMT>
+__global__ __launch_bounds__(512) void gemm_streamk_kernel(GemmArgs g, float *part, int units) {
+  constexpr int R = 16 * MT;     // A rows staged (rows past m repeat row m-1)
+  constexpr int kCopies = R / 8; // 1 KB copies per unit (8 rows each)
+  __shared__ __attribute__((aligned(1024))) uint8_t atile[UPW * R * kBK];
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t m = g.m, n = g.n;
+  const int KB = (int)(g.k / kBK);
+  const int w = (int)blockIdx.x, u0 = w * UPW, nu = min(UPW, units - u0);   // nu >= 1 (host plan)
+  const int t0 = u0 / KB;
+
+  // per unit j (units past the share repeat its last one): tile, K block, scales
+  int ut[UPW], ukb[UPW];
+  float sa[UPW][MT], sb[UPW];
+#pragma unroll
+  for (int j = 0; j < UPW; ++j) {
+    const int u = u0 + min(j, nu - 1);
+    ut[j] = u / KB;
+    ukb[j] = u - ut[j] * KB;
+    sb[j] = g.sb[(int64_t)ut[j] * g.sb_ld + ukb[j]];
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+      sa[j][i] = load_sa<SA_FMT>(g.sa, g.sa_ld, min((int64_t)(16 * i + (lane & 15)), m - 1), ukb[j]);
+  }
+  // A of every unit -> LDS: wave wv fills copy wv % kCopies of each unit (slot s of a
+  // copy: row s/8 of its 8, physical chunk s%8 holding logical chunk (s%8)^swz_key(row));
+  // waves past kCopies repeat a copy, so each wave issues exactly UPW copies.
+  {
+    const int q = wv % kCopies, slot = 64 * q + lane;
+    const int row = slot >> 3, chunk = (slot & 7) ^ swz_key(row);
+    const uint32_t off = (uint32_t)(min((int64_t)row, m - 1) * g.lda) + (uint32_t)(chunk * 16);
+#pragma unroll
+    for (int j = 0; j < UPW; ++j) load_lds16(g.A + (int64_t)ukb[j] * kBK, off, atile + j * (R * kBK) + 1024 * q);
+  }
+  // B: this wave's 16 columns of each unit, 32 K bytes per lane (the frag() layout)
+  v8i bfr[UPW];
+#pragma unroll
+  for (int j = 0; j < UPW; ++j) {
+    const int64_t col = min((int64_t)ut[j] * 128 + 16 * wv + (lane & 15), n - 1);
+    const uint8_t *pb = g.B + col * g.ldb + (int64_t)ukb[j] * kBK + 32 * (lane >> 4);
+    const u32x4 lo = *reinterpret_cast<const u32x4 *>(pb);
+    const u32x4 hi = *reinterpret_cast<const u32x4 *>(pb + 16);
+    bfr[j] = (v8i){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  }
+
+  v4f acc[MT], head[MT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i) acc[i] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+  const int64_t ccol = 16 * wv + 4 * (lane >> 4);   // this lane's first column within a tile
+  // sharers of tile t: the workgroups whose shares meet its units
+  auto wlo_of = [&](int t) { return (int)((int64_t)t * KB / UPW); };
+  auto whi_of = [&](int t) { return (int)(((int64_t)t * KB + KB - 1) / UPW); };
+  bool has_head = false, stored = false;   // workgroup-uniform
+#pragma unroll
+  for (int j = 0; j < UPW; ++j) {
+    // unit j's A copies have landed in every wave once each wave has at most the later
+    // units' copies and all B loads outstanding (the compiler waits for bfr[j] itself);
+    // after a store the count no longer holds, and the wait is for everything
+    vm_wait_barrier(stored ? 0 : (UPW - 1 - j) + 2 * UPW);
+    if (j >= nu) continue;   // workgroup-uniform
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      const v4f p = mfma_k128(bfr[j], frag(atile + j * (R * kBK), 16 * i + (lane & 15), lane));
+      const float c = sa[j][i] * sb[j];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[i][r] = __builtin_fmaf(p[r], c, acc[i][r]);
+    }
+    if (j == nu - 1 || ukb[j] != KB - 1) continue;   // the share's last segment stays in acc
+    const int t = ut[j];
+    if (wlo_of(t) == whi_of(t)) {
+      // a whole tile: round and store
+      uint16_t *dt = reinterpret_cast<uint16_t *>(g.D) + (int64_t)t * 128;
+#pragma unroll
+      for (int i = 0; i < MT; ++i) {
+        const int64_t row = 16 * i + (lane & 15), col = (int64_t)t * 128 + ccol;
+        if (row < m && col < n) store_bf16x4(dt + row * g.ldd + ccol, acc[i], n - col);
+      }
+      stored = true;
+    } else {
+      // the share's first tile, shared with earlier workgroups: its partial waits in head
+#pragma unroll
+      for (int i = 0; i < MT; ++i) head[i] = acc[i];
+      has_head = true;
+    }
+#pragma unroll
+    for (int i = 0; i < MT; ++i) acc[i] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+  }
+
+  // the share's last segment, tile t1: a whole tile, or shared
+  const int t1 = (u0 + nu - 1) / KB;
+  const bool tail_shared = wlo_of(t1) != whi_of(t1);
+  if (!tail_shared) {
+    uint16_t *dt = reinterpret_cast<uint16_t *>(g.D) + (int64_t)t1 * 128;
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      const int64_t row = 16 * i + (lane & 15), col = (int64_t)t1 * 128 + ccol;
+      if (row < m && col < n) store_bf16x4(dt + row * g.ldd + ccol, acc[i], n - col);
+    }
+  }
+  if (!has_head && !tail_shared) return;   // workgroup-uniform
+
+  // partial sums: slot 2w holds the share's first tile t0, slot 2w+1 its last tile when
+  // that is another one
+  constexpr int kSlot = 8 * MT * 64 * 4;   // floats
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    if (h == 0 ? !has_head : !tail_shared) continue;
+    v4f *ps = reinterpret_cast<v4f *>(part + (int64_t)(h == 0 || t1 == t0 ? 2 * w : 2 * w + 1) * kSlot) +
+              wv * MT * 64 + lane;
+#pragma unroll
+    for (int i = 0; i < MT; ++i) ps[i * 64] = h == 0 ? head[i] : acc[i];
+  }
+}
+
+// D tile t (when shared) = bf16(sum of its sharers' partial sums in workgroup order).
+// Workgroup (t, i) adds row subtile i: thread (wave v, lane l) the four columns that
+// wave v's lane l held in gemm_streamk_kernel, eight sharers' loads in flight.
+template <int MT>
+__global__ __launch_bounds__(512) void streamk_fixup_kernel(GemmArgs g, const float *part, int upw) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int t = (int)blockIdx.x / MT, i = (int)blockIdx.x % MT;
+  const int KB = (int)(g.k / kBK);
+  const int wlo = (int)((int64_t)t * KB / upw), whi = (int)(((int64_t)t * KB + KB - 1) / upw);
+  const int64_t row = 16 * i + (lane & 15), col = (int64_t)t * 128 + 16 * wv + 4 * (lane >> 4);
+  if (wlo == whi || row >= g.m || col >= g.n) return;   // a whole tile is stored already
+  constexpr int kSlot = 8 * MT * 64 * 4;
+  const int64_t off = (int64_t)(wv * MT + i) * 64 + lane;   // v4f index within a slot
+  v4f sum = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+  for (int w0 = wlo; w0 <= whi; w0 += 8) {
+    v4f v[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int ww = min(w0 + q, whi);
+      const int slot = (int)((int64_t)ww * upw / KB) == t ? 2 * ww : 2 * ww + 1;
+      v[q] = reinterpret_cast<const v4f *>(part + (int64_t)slot * kSlot)[off];
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      if (w0 + q <= whi) sum += v[q];
+  }
+  store_bf16x4(reinterpret_cast<uint16_t *>(g.D) + row * g.ldd + col, sum, g.n - col);
+}
+
 }  // namespace
 
 // Compute units of the current device (queried once per device).
@@ -1067,4 +1256,54 @@ hipError_t launch_gemm(const GemmArgs &a, hipStream_t st) {
   return launch_cfg<Cfg<2, 2, 2>>(a, st);
 }
 
+// Stream-K plan for m <= 64: units = 128-column tiles x K blocks; UPW units per
+// workgroup, the fewest (at most 8) that keep the workgroups within one per CU of
+// the 256-CU part (more than 256 only when that takes over 8 units each).
+SplitKPlan splitk_plan(int64_t m, int64_t n, int64_t k) {
+  SplitKPlan p;
+  p.tiles_n = (n + 127) / 128;
+  p.units = p.tiles_n * (k / kBK);
+  p.upw = std::min<int64_t>(8, std::max<int64_t>(1, (p.units + kStreamKSlots - 1) / kStreamKSlots));
+  p.grid = (p.units + p.upw - 1) / p.upw;
+  // two slots per workgroup of the 16*MT x 128 fp32 of a tile (MT = ceil(m/16), 1, 2 or 4)
+  const int64_t rows = m <= 16 ? 16 : m <= 32 ? 32 : 64;
+  p.workspace_bytes = 2 * p.grid * rows * 128 * (int64_t)sizeof(float);
+  return p;
+}
+
+template <int MT, int UPW>
+static void launch_streamk_cfg(const GemmArgs &a, float *part, const SplitKPlan &p, hipStream_t st) {
+  const dim3 grid((unsigned)p.grid);
+  if (a.sa_fmt == kSfPackedUe8m0)
+    hipLaunchKernelGGL((gemm_streamk_kernel<MT, UPW, kSfPackedUe8m0>), grid, dim3(512), 0, st, a, part, (int)p.units);
+  else
+    hipLaunchKernelGGL((gemm_streamk_kernel<MT, UPW, kSfFp32>), grid, dim3(512), 0, st, a, part, (int)p.units);
+}
+
+template <int MT>
+static void launch_streamk_mt(const GemmArgs &a, float *part, const SplitKPlan &p, hipStream_t st) {
+  switch (p.upw) {
+    case 1: launch_streamk_cfg<MT, 1>(a, part, p, st); break;
+    case 2: launch_streamk_cfg<MT, 2>(a, part, p, st); break;
+    case 3: launch_streamk_cfg<MT, 3>(a, part, p, st); break;
+    case 4: launch_streamk_cfg<MT, 4>(a, part, p, st); break;
+    case 5: launch_streamk_cfg<MT, 5>(a, part, p, st); break;
+    case 6: launch_streamk_cfg<MT, 6>(a, part, p, st); break;
+    case 7: launch_streamk_cfg<MT, 7>(a, part, p, st); break;
+    default: launch_streamk_cfg<MT, 8>(a, part, p, st); break;
+  }
+  // shared tiles: one workgroup per row subtile; none is shared when every share holds
+  // whole tiles (UPW a multiple of KB)
+  if (p.upw % (a.k / kBK) != 0)
+    hipLaunchKernelGGL(streamk_fixup_kernel<MT>, dim3((unsigned)(p.tiles_n * MT)), dim3(512), 0, st, a, part,
+                       (int)p.upw);
+}
+
+hipError_t launch_gemm_splitk(const GemmArgs &a, void *ws, const SplitKPlan &p, hipStream_t st) {
+  float *part = static_cast<float *>(ws);
+  if (a.m <= 16) launch_streamk_mt<1>(a, part, p, st);
+  else if (a.m <= 32) launch_streamk_mt<2>(a, part, p, st);
+  else launch_streamk_mt<4>(a, part, p, st);
+  return hipGetLastError();
+}
 }  // namespace fgfp8

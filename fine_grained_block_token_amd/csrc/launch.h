@@ -97,6 +97,15 @@ hipError_t launch_cast_per_token(const CastTokenArgs &a, hipStream_t st);
 hipError_t launch_cast_per_block(const CastBlockArgs &a, hipStream_t st);
 hipError_t launch_cast_dual(const CastDualArgs &a, hipStream_t st);
 hipError_t launch_gemm(const GemmArgs &a, hipStream_t st);
+
+// Stream-K decode GEMM (m <= 64, bf16 output).  Workspace: 2*grid slots of
+// 16*ceil(m/16) x 128 fp32 partial sums.
+constexpr int64_t kStreamKSlots = 256;   // workgroups the plan aims at (one per CU)
+struct SplitKPlan {
+  int64_t tiles_n, units, upw, grid, workspace_bytes;
+};
+SplitKPlan splitk_plan(int64_t m, int64_t n, int64_t k);
+hipError_t launch_gemm_splitk(const GemmArgs &a, void *ws, const SplitKPlan &p, hipStream_t st);
 // UE8M0 group-32 recipe: sa and sb are packed words (one per row and 128-K block,
 // MN-major: (i, kb) at sa[kb*sa_ld + i], (j, kb) at sb[kb*sb_ld + j]).
 hipError_t launch_gemm_g32(const GemmArgs &a, hipStream_t st);

@@ -184,6 +184,45 @@ int gemm_fp8_nt_bf16(const uint8_t *A, int64_t lda, const void *sa, int sa_fmt, 
                      void *stream);
 
 /*
+ * gemm_fp8_nt_bf16_splitk -- the same product as gemm_fp8_nt_bf16 (same
+ * definition, passages and operand layouts), for decode-sized m <= 64, with
+ * K split over workgroups ("DeepGEMM Essentials", Part 14: at these sizes the
+ * product is bound by reading B once, so the work is spread evenly over the
+ * compute units).  The K blocks of all 128-column tiles are dealt out in equal
+ * consecutive shares, one per workgroup; a tile that a share covers whole is
+ * rounded and stored at once, and a tile split between shares gets the fp32
+ * promoted partial sums of its shares added in share order by a second kernel
+ * (deterministic: the same inputs give the same bits on every call), then
+ * rounded to bf16.  Each share's sum follows the definition above block by
+ * block; only the grouping of the fp32 additions over K blocks differs from
+ * gemm_fp8_nt_bf16, so the two agree to fp32 rounding, not bit for bit.
+ *
+ * workspace        device memory, 16-byte aligned, at least
+ *                  gemm_fp8_nt_bf16_splitk_workspace(m, n, k) bytes, owned by
+ *                  the caller; its contents on entry do not matter and are
+ *                  overwritten.  Calls that share a workspace must be ordered
+ *                  (one stream, or events): two in flight at once race.
+ * m                0 <= m <= 64 (FGFP8_EINVAL above 64).
+ * Other arguments, errors and k, n as gemm_fp8_nt_bf16; also FGFP8_EINVAL
+ * when ceil(n/128) * k/128 exceeds 2^31 - 16.
+ */
+int gemm_fp8_nt_bf16_splitk(const uint8_t *A, int64_t lda, const void *sa, int sa_fmt, int64_t sa_ld,
+                            const uint8_t *B, int64_t ldb, const float *sb, int64_t sb_ld,
+                            uint16_t *D, int64_t ldd, int64_t m, int64_t n, int64_t k,
+                            void *workspace, int64_t workspace_bytes, void *stream);
+
+/*
+ * gemm_fp8_nt_bf16_splitk_workspace -- bytes of workspace that
+ * gemm_fp8_nt_bf16_splitk needs for (m, n, k): 2 * G * 16*ceil(m/16) * 128 * 4
+ * (two partial-sum slots per workgroup), G the number of workgroups (which
+ * depends on n and k only).  0 when m or n is 0; FGFP8_EINVAL (-1) when m is
+ * outside 0..64, n < 0, k is not a positive multiple of 128, or
+ * ceil(n/128) * k/128 exceeds 2^31 - 16.  Host only: launches nothing and
+ * needs no device.
+ */
+int64_t gemm_fp8_nt_bf16_splitk_workspace(int64_t m, int64_t n, int64_t k);
+
+/*
  * gemm_fp8_nt_bf16_cast -- gemm_fp8_nt_bf16 with the per-token FP8 cast of its
  * output fused into the epilogue, so that the next layer's FP8 operand leaves
  * the GEMM directly ("[Help] Starter script for nn.Linear for fwd,bwd": the

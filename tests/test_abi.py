@@ -29,7 +29,8 @@ def test_header_declares_the_entry_points():
               "wgrad_gemm_fp8_nt_fp32", "m_grouped_gemm_fp8_nt_bf16_contiguous", "gemm_fp8_nt_bf16_cast",
               "gemm_fp8_nt_bf16_ue8m0_g32", "wgrad_gemm_fp8_nt_fp32_ue8m0_g32",
               "m_grouped_gemm_fp8_nt_bf16_ue8m0_g32_contiguous", "wgrad_gemm_fp8_nt_fp32_ue8m0",
-              "gemm_fp8_nt_bf16_ue8m0", "fgfp8_status_string"):
+              "gemm_fp8_nt_bf16_ue8m0", "gemm_fp8_nt_bf16_splitk", "gemm_fp8_nt_bf16_splitk_workspace",
+              "fgfp8_status_string"):
         assert f in names
 
 
@@ -284,3 +285,47 @@ def test_gemm_ue8m0_rejects(lib, kw):
 
 def test_gemm_ue8m0_zero_size_is_ok(lib):
     assert gue(lib, m=0) == 0 and gue(lib, n=0, fmt=2) == 0
+
+
+def splitk(lib, **kw):
+    a = dict(A=P, lda=256, sa=S, fmt=0, sald=64, B=Q, ldb=256, sb=S, sbld=2, D=P, ldd=256, m=64, n=256, k=256,
+             ws=ctypes.c_void_p(0x40000), wsb=1 << 20, st=None)
+    a.update(kw)
+    return lib.gemm_fp8_nt_bf16_splitk(a["A"], a["lda"], a["sa"], a["fmt"], a["sald"], a["B"], a["ldb"], a["sb"],
+                                       a["sbld"], a["D"], a["ldd"], a["m"], a["n"], a["k"], a["ws"], a["wsb"],
+                                       a["st"])
+
+
+@pytest.mark.parametrize("kw", [
+    dict(m=65, sald=65), dict(k=200), dict(k=0), dict(lda=200), dict(sbld=1), dict(ldd=252), dict(fmt=5),
+    dict(A=None), dict(ws=None), dict(ws=ctypes.c_void_p(0x40008)), dict(wsb=2 * 4 * 64 * 512 - 4),
+    dict(D=ctypes.c_void_p(0x10004)), dict(m=-1),
+])
+def test_splitk_rejects(lib, kw):
+    assert splitk(lib, **kw) == -1
+
+
+def test_splitk_zero_size_is_ok(lib):
+    assert splitk(lib, m=0, ws=None, wsb=0) == 0 and splitk(lib, n=0, ws=None, wsb=0) == 0
+
+
+def test_splitk_workspace_size(lib):
+    ws = lib.gemm_fp8_nt_bf16_splitk_workspace
+    assert ws(0, 4096, 7168) == 0 and ws(64, 0, 7168) == 0
+    for bad in [(65, 4096, 7168), (-1, 4096, 7168), (64, -1, 7168), (64, 4096, 0), (64, 4096, 100),
+                (64, 1 << 40, 128 * 1024)]:
+        assert ws(*bad) == -1
+    # two partial-sum slots per workgroup of 16*ceil(m/16) x 128 fp32 (16, 32 or 64 rows); the
+    # workgroup count depends on n and k only, at least one per 8 units (128-column tile x K
+    # block) and at most one per unit
+    for n, k in [(7168, 4096), (4096, 7168), (1000, 128), (130, 384), (9000, 256), (38400, 256)]:
+        units = -(-n // 128) * (k // 128)
+        for m, rows in ((1, 16), (16, 16), (17, 32), (32, 32), (33, 64), (64, 64)):
+            b = ws(m, n, k)
+            assert b % (2 * rows * 512) == 0
+            g = b // (2 * rows * 512)
+            assert -(-units // 8) <= g <= units
+            assert g == ws(1, n, k) // (2 * 16 * 512)
+    # the decode shapes: 1792 units in 256 shares of 7
+    assert ws(64, 7168, 4096) == 2 * 256 * 64 * 512
+    assert ws(64, 4096, 7168) == 2 * 256 * 64 * 512
