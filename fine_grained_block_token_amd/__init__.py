@@ -55,13 +55,14 @@ def load():
     lib.m_grouped_gemm_fp8_nt_bf16_contiguous.argtypes = [p, i64, p, i32, i64, p, i64, i64, p, i64, i64, p, i64,
                                                           p, i64, i64, i64, i64, p]
     lib.gemm_fp8_nt_bf16_splitk.argtypes = [p, i64, p, i32, i64, p, i64, p, i64, p, i64, i64, i64, i64, p, i64, p]
+    lib.gemm_fp8_nt_bf16_splitk_noalloc.argtypes = [p, i64, p, i32, i64, p, i64, p, i64, p, i64, i64, i64, i64, p]
     lib.gemm_fp8_nt_bf16_splitk_workspace.argtypes = [i64, i64, i64]
     lib.gemm_fp8_nt_bf16_splitk_workspace.restype = i64
     for f in ("cast_per_token", "cast_per_block", "cast_per_token_dual", "gemm_fp8_nt_bf16",
               "wgrad_gemm_fp8_nt_fp32", "m_grouped_gemm_fp8_nt_bf16_contiguous", "gemm_fp8_nt_bf16_cast",
               "gemm_fp8_nt_bf16_ue8m0_g32", "wgrad_gemm_fp8_nt_fp32_ue8m0_g32",
               "m_grouped_gemm_fp8_nt_bf16_ue8m0_g32_contiguous", "wgrad_gemm_fp8_nt_fp32_ue8m0",
-              "gemm_fp8_nt_bf16_ue8m0", "gemm_fp8_nt_bf16_splitk"):
+              "gemm_fp8_nt_bf16_ue8m0", "gemm_fp8_nt_bf16_splitk", "gemm_fp8_nt_bf16_splitk_noalloc"):
         getattr(lib, f).restype = i32
     lib.fgfp8_status_string.argtypes = [i32]
     lib.fgfp8_status_string.restype = ctypes.c_char_p
@@ -74,7 +75,7 @@ EXPORTED = ("cast_per_token", "cast_per_block", "cast_per_token_dual", "gemm_fp8
             "gemm_fp8_nt_bf16_ue8m0_g32", "wgrad_gemm_fp8_nt_fp32_ue8m0_g32",
             "m_grouped_gemm_fp8_nt_bf16_ue8m0_g32_contiguous", "wgrad_gemm_fp8_nt_fp32_ue8m0",
             "gemm_fp8_nt_bf16_ue8m0", "gemm_fp8_nt_bf16_splitk", "gemm_fp8_nt_bf16_splitk_workspace",
-            "fgfp8_status_string")
+            "gemm_fp8_nt_bf16_splitk_noalloc", "fgfp8_status_string")
 
 
 def _check(rc: int, what: str):
@@ -199,6 +200,22 @@ def gemm_fp8_nt_bf16_splitk(A: torch.Tensor, sa: torch.Tensor, B: torch.Tensor, 
                                           _ptr(sb), sb.stride(0), _ptr(D), D.stride(0), m, n, k, _ptr(workspace),
                                           workspace.numel() * workspace.element_size(), _stream(A)),
            "gemm_fp8_nt_bf16_splitk")
+
+
+def gemm_fp8_nt_bf16_splitk_noalloc(A: torch.Tensor, sa: torch.Tensor, B: torch.Tensor, sb: torch.Tensor,
+                                    D: torch.Tensor, sa_fmt: int = SF_FP32) -> None:
+    """gemm_fp8_nt_bf16_splitk with the library's static 32 MiB device scratch in place of a workspace
+    (allocates nothing; calls that overlap on one GPU race)."""
+    A, B = _u8(A), _u8(B)
+    m, k = A.shape
+    n = B.shape[0]
+    if sa.shape[0] > 1 and sa.stride(0) != 1:
+        raise ValueError("sa must be MN-major (stride(0) == 1)")
+    sa_ld = sa.stride(1) if sa.dim() == 2 else m
+    _check(load().gemm_fp8_nt_bf16_splitk_noalloc(_ptr(A), A.stride(0), _ptr(sa), sa_fmt, sa_ld, _ptr(B),
+                                                  B.stride(0), _ptr(sb), sb.stride(0), _ptr(D), D.stride(0), m, n, k,
+                                                  _stream(A)),
+           "gemm_fp8_nt_bf16_splitk_noalloc")
 
 
 def gemm_fp8_nt_bf16_cast(A: torch.Tensor, sa: torch.Tensor, B: torch.Tensor, sb: torch.Tensor,

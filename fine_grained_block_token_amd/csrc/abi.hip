@@ -38,6 +38,23 @@ int check_device() {
 
 int launched(hipError_t e) { return e == hipSuccess ? FGFP8_OK : FGFP8_ELAUNCH; }
 
+// The partial sums of gemm_fp8_nt_bf16_splitk_noalloc: one copy of this array per
+// GPU, allocated by the runtime when the library's code object is loaded there and
+// held until the process ends.  Host code never uses the name itself (on the host it
+// is only a stand-in): the device address comes from hipGetSymbolAddress, per device.
+static __device__ __align__(256) uint8_t scratch[FGFP8_SCRATCH_BYTES];
+
+std::atomic<void *> g_scratch_ptr[64];
+
+// Device address of `scratch` on device `dev` (the current device), looked up once.
+void *scratch_ptr(int dev) {
+  void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+  g_scratch_ptr[dev].store(p, std::memory_order_release);
+  return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -187,6 +204,28 @@ int gemm_fp8_nt_bf16_splitk(const uint8_t *A, int64_t lda, const void *sa, int s
   if (dev != FGFP8_OK) return dev;
   fgfp8::GemmArgs a{A, lda, sa, sa_fmt, sa_ld, B, ldb, sb, sb_ld, D, ldd, m, n, k, false};
   return launched(fgfp8::launch_gemm_splitk(a, workspace, plan, static_cast<hipStream_t>(stream)));
+}
+
+int gemm_fp8_nt_bf16_splitk_noalloc(const uint8_t *A, int64_t lda, const void *sa, int sa_fmt, int64_t sa_ld,
+                                    const uint8_t *B, int64_t ldb, const float *sb, int64_t sb_ld, uint16_t *D,
+                                    int64_t ldd, int64_t m, int64_t n, int64_t k, void *stream) {
+  if (sa_fmt != kSfFp32 && sa_fmt != kSfUe8m0 && sa_fmt != kSfPackedUe8m0) return FGFP8_EINVAL;
+  if (m > 64) return FGFP8_EINVAL;
+  const int c = check_gemm_common(A, lda, sa, sa_ld, B, ldb, sb, D, m, n, k);
+  if (c != 1) return c;
+  if (sb_ld < k / 128) return FGFP8_EINVAL;
+  if (!aligned(D, 16) || ldd < n || ldd % 8 != 0) return FGFP8_EINVAL;
+  if (cdiv(n, 128) * (k / 128) > 0x7FFFFFF0) return FGFP8_EINVAL;
+  const fgfp8::SplitKPlan plan = fgfp8::splitk_plan(m, n, k);
+  if (plan.workspace_bytes > FGFP8_SCRATCH_BYTES) return FGFP8_ESCRATCH;
+  const int dev = check_device();
+  if (dev != FGFP8_OK) return dev;
+  int d = -1;
+  if (hipGetDevice(&d) != hipSuccess || d < 0 || d >= 64) return FGFP8_EDEVICE;
+  void *ws = scratch_ptr(d);
+  if (!ws) return FGFP8_EDEVICE;
+  fgfp8::GemmArgs a{A, lda, sa, sa_fmt, sa_ld, B, ldb, sb, sb_ld, D, ldd, m, n, k, false};
+  return launched(fgfp8::launch_gemm_splitk(a, ws, plan, static_cast<hipStream_t>(stream)));
 }
 
 int gemm_fp8_nt_bf16_cast(const uint8_t *A, int64_t lda, const void *sa, int sa_fmt, int64_t sa_ld,
@@ -341,6 +380,7 @@ const char *fgfp8_status_string(int status) {
     case FGFP8_EINVAL: return "invalid argument (nothing launched)";
     case FGFP8_EDEVICE: return "current device is not gfx950";
     case FGFP8_ELAUNCH: return "kernel launch failed";
+    case FGFP8_ESCRATCH: return "problem needs more than the 32 MiB static scratch (nothing launched)";
     default: return "unknown status";
   }
 }

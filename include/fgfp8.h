@@ -4,8 +4,10 @@
  *
  * Plain C: pointers, sizes and an opaque stream.  Every pointer named as a
  * tensor below is DEVICE memory owned by the caller; the library allocates
- * nothing and keeps no state beyond a per-device "is this gfx950" check and
- * the runtime's occupancy figures for its persistent cast kernels.
+ * nothing at run time and keeps no state beyond a per-device "is this gfx950"
+ * check, the runtime's occupancy figures for its persistent cast kernels, and
+ * the static device array of gemm_fp8_nt_bf16_splitk_noalloc (32 MiB on each
+ * GPU the library is loaded on, held until the process ends).
  * `stream` is a hipStream_t passed as void* (NULL = the default stream).
  * Every call is asynchronous and stream-ordered; none synchronises the host.
  *
@@ -15,6 +17,9 @@
  *                       launch: nothing was written
  *   FGFP8_EDEVICE (-2)  the current device is not gfx950 (or no device)
  *   FGFP8_ELAUNCH (-3)  the kernel launch failed (hipGetLastError)
+ *   FGFP8_ESCRATCH (-4) gemm_fp8_nt_bf16_splitk_noalloc only: the problem
+ *                       needs more than the library's static scratch
+ *                       (FGFP8_SCRATCH_BYTES); nothing was written
  * Nothing aborts, throws or prints.
  *
  * Formats.  E4M3 is the OCP FP8 "fn" format (bias 7, largest finite 448, no
@@ -47,6 +52,10 @@ extern "C" {
 #define FGFP8_EINVAL (-1)
 #define FGFP8_EDEVICE (-2)
 #define FGFP8_ELAUNCH (-3)
+#define FGFP8_ESCRATCH (-4)
+
+/* bytes of the static device scratch of gemm_fp8_nt_bf16_splitk_noalloc */
+#define FGFP8_SCRATCH_BYTES (32LL << 20)
 
 #define FGFP8_IN_BF16 0
 #define FGFP8_IN_FP32 1
@@ -221,6 +230,28 @@ int gemm_fp8_nt_bf16_splitk(const uint8_t *A, int64_t lda, const void *sa, int s
  * needs no device.
  */
 int64_t gemm_fp8_nt_bf16_splitk_workspace(int64_t m, int64_t n, int64_t k);
+
+/*
+ * gemm_fp8_nt_bf16_splitk_noalloc -- gemm_fp8_nt_bf16_splitk without a
+ * workspace argument, for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  The partial sums go to a static device array of the library
+ * (FGFP8_SCRATCH_BYTES = 32 MiB per GPU, present from the library's load until
+ * the process ends); the call itself allocates nothing.  Same kernels and
+ * result bits as gemm_fp8_nt_bf16_splitk with a workspace.
+ *
+ * Limit: gemm_fp8_nt_bf16_splitk_workspace(m, n, k) must not exceed
+ * FGFP8_SCRATCH_BYTES (for m = 64 up to about 3600 units of 128 columns x 128
+ * K, e.g. n = k = 7168), else FGFP8_ESCRATCH and nothing is written.
+ * Every call on a GPU shares that GPU's array: calls that overlap on one GPU
+ * (two streams, or two threads) race and give wrong results, so order them.
+ * Nothing in the array has to start at any value: each call writes every
+ * partial sum before it reads it.
+ * Arguments, layouts and the other errors as gemm_fp8_nt_bf16_splitk.
+ */
+int gemm_fp8_nt_bf16_splitk_noalloc(const uint8_t *A, int64_t lda, const void *sa, int sa_fmt, int64_t sa_ld,
+                                    const uint8_t *B, int64_t ldb, const float *sb, int64_t sb_ld,
+                                    uint16_t *D, int64_t ldd, int64_t m, int64_t n, int64_t k, void *stream);
 
 /*
  * gemm_fp8_nt_bf16_cast -- gemm_fp8_nt_bf16 with the per-token FP8 cast of its

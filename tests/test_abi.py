@@ -30,7 +30,7 @@ def test_header_declares_the_entry_points():
               "gemm_fp8_nt_bf16_ue8m0_g32", "wgrad_gemm_fp8_nt_fp32_ue8m0_g32",
               "m_grouped_gemm_fp8_nt_bf16_ue8m0_g32_contiguous", "wgrad_gemm_fp8_nt_fp32_ue8m0",
               "gemm_fp8_nt_bf16_ue8m0", "gemm_fp8_nt_bf16_splitk", "gemm_fp8_nt_bf16_splitk_workspace",
-              "fgfp8_status_string"):
+              "gemm_fp8_nt_bf16_splitk_noalloc", "fgfp8_status_string"):
         assert f in names
 
 
@@ -40,9 +40,10 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings(lib):
-    for rc in (0, -1, -2, -3):
+    for rc in (0, -1, -2, -3, -4):
         assert lib.fgfp8_status_string(rc)
     assert b"invalid" in lib.fgfp8_status_string(-1)
+    assert b"scratch" in lib.fgfp8_status_string(-4)
 
 
 # fake but 16-byte aligned addresses: validation rejects before any access
@@ -329,3 +330,26 @@ def test_splitk_workspace_size(lib):
     # the decode shapes: 1792 units in 256 shares of 7
     assert ws(64, 7168, 4096) == 2 * 256 * 64 * 512
     assert ws(64, 4096, 7168) == 2 * 256 * 64 * 512
+
+
+def noalloc(lib, **kw):
+    a = dict(A=P, lda=7168, sa=S, fmt=0, sald=64, B=Q, ldb=7168, sb=S, sbld=56, D=P, ldd=7168, m=64, n=7168,
+             k=7168, st=None)
+    a.update(kw)
+    return lib.gemm_fp8_nt_bf16_splitk_noalloc(a["A"], a["lda"], a["sa"], a["fmt"], a["sald"], a["B"], a["ldb"],
+                                               a["sb"], a["sbld"], a["D"], a["ldd"], a["m"], a["n"], a["k"], a["st"])
+
+
+@pytest.mark.parametrize("kw", [dict(m=65, sald=65), dict(k=200), dict(lda=200), dict(sbld=1), dict(ldd=7164),
+                                dict(fmt=5), dict(A=None), dict(D=ctypes.c_void_p(0x10004)), dict(m=-1)])
+def test_splitk_noalloc_rejects(lib, kw):
+    assert noalloc(lib, **kw) == -1
+
+
+def test_splitk_noalloc_scratch_limit(lib):
+    # 64 x 7168 x 16384 needs 58.7 MB of partial sums, beyond the 32 MiB static scratch: refused on
+    # the host (FGFP8_ESCRATCH) before any device call; zero sizes are accepted
+    assert lib.gemm_fp8_nt_bf16_splitk_workspace(64, 7168, 16384) > 32 << 20
+    assert noalloc(lib, k=16384, lda=16384, ldb=16384, sbld=128) == -4
+    assert lib.gemm_fp8_nt_bf16_splitk_workspace(64, 7168, 7168) <= 32 << 20
+    assert noalloc(lib, m=0) == 0 and noalloc(lib, n=0) == 0
