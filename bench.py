@@ -44,8 +44,10 @@ def mfma_peak(op):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=30)
+    # the GPU's clocks settle over the first ~12 steps (the weight gradient runs 630 us in the
+    # first step and 480-500 us from about the twelfth on), so the default warm-up covers them
+    ap.add_argument("--warmup", type=int, default=15)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--calibration-copy", type=int, default=0, metavar="MIB",
