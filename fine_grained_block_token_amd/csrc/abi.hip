@@ -183,7 +183,7 @@ int gemm_fp8_nt_bf16(const uint8_t *A, int64_t lda, const void *sa, int sa_fmt, 
 int64_t gemm_fp8_nt_bf16_splitk_workspace(int64_t m, int64_t n, int64_t k) {
   if (m < 0 || m > 64 || n < 0 || k <= 0 || k % 128 != 0) return FGFP8_EINVAL;
   if (m == 0 || n == 0) return 0;
-  if (cdiv(n, 128) * (k / 128) > 0x7FFFFFF0) return FGFP8_EINVAL;
+  if (cdiv(n, 128) * (k / 128) > 0x7FFFFFF0 || cdiv(n, 128) > 0x1FFFFFFF) return FGFP8_EINVAL;
   return fgfp8::splitk_plan(m, n, k).workspace_bytes;
 }
 
@@ -197,7 +197,8 @@ int gemm_fp8_nt_bf16_splitk(const uint8_t *A, int64_t lda, const void *sa, int s
   if (c != 1) return c;
   if (sb_ld < k / 128) return FGFP8_EINVAL;
   if (!aligned(D, 16) || ldd < n || ldd % 8 != 0) return FGFP8_EINVAL;
-  if (cdiv(n, 128) * (k / 128) > 0x7FFFFFF0) return FGFP8_EINVAL;   // unit indices are 32-bit
+  // unit indices are 32-bit, and so is the fix-up grid (up to 4 workgroups per 128-column tile)
+  if (cdiv(n, 128) * (k / 128) > 0x7FFFFFF0 || cdiv(n, 128) > 0x1FFFFFFF) return FGFP8_EINVAL;
   const fgfp8::SplitKPlan plan = fgfp8::splitk_plan(m, n, k);
   if (!workspace || !aligned(workspace, 16) || workspace_bytes < plan.workspace_bytes) return FGFP8_EINVAL;
   const int dev = check_device();
@@ -215,7 +216,7 @@ int gemm_fp8_nt_bf16_splitk_noalloc(const uint8_t *A, int64_t lda, const void *s
   if (c != 1) return c;
   if (sb_ld < k / 128) return FGFP8_EINVAL;
   if (!aligned(D, 16) || ldd < n || ldd % 8 != 0) return FGFP8_EINVAL;
-  if (cdiv(n, 128) * (k / 128) > 0x7FFFFFF0) return FGFP8_EINVAL;
+  if (cdiv(n, 128) * (k / 128) > 0x7FFFFFF0 || cdiv(n, 128) > 0x1FFFFFFF) return FGFP8_EINVAL;
   const fgfp8::SplitKPlan plan = fgfp8::splitk_plan(m, n, k);
   if (plan.workspace_bytes > FGFP8_SCRATCH_BYTES) return FGFP8_ESCRATCH;
   const int dev = check_device();

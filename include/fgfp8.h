@@ -213,7 +213,7 @@ int gemm_fp8_nt_bf16(const uint8_t *A, int64_t lda, const void *sa, int sa_fmt, 
  *                  (one stream, or events): two in flight at once race.
  * m                0 <= m <= 64 (FGFP8_EINVAL above 64).
  * Other arguments, errors and k, n as gemm_fp8_nt_bf16; also FGFP8_EINVAL
- * when ceil(n/128) * k/128 exceeds 2^31 - 16.
+ * when ceil(n/128) * k/128 exceeds 2^31 - 16 or ceil(n/128) exceeds 2^29 - 1.
  */
 int gemm_fp8_nt_bf16_splitk(const uint8_t *A, int64_t lda, const void *sa, int sa_fmt, int64_t sa_ld,
                             const uint8_t *B, int64_t ldb, const float *sb, int64_t sb_ld,
@@ -225,9 +225,9 @@ int gemm_fp8_nt_bf16_splitk(const uint8_t *A, int64_t lda, const void *sa, int s
  * gemm_fp8_nt_bf16_splitk needs for (m, n, k): 2 * G * 16*ceil(m/16) * 128 * 4
  * (two partial-sum slots per workgroup), G the number of workgroups (which
  * depends on n and k only).  0 when m or n is 0; FGFP8_EINVAL (-1) when m is
- * outside 0..64, n < 0, k is not a positive multiple of 128, or
- * ceil(n/128) * k/128 exceeds 2^31 - 16.  Host only: launches nothing and
- * needs no device.
+ * outside 0..64, n < 0, k is not a positive multiple of 128, or the limits
+ * of gemm_fp8_nt_bf16_splitk on n and k are exceeded.  Host only: launches
+ * nothing and needs no device.
  */
 int64_t gemm_fp8_nt_bf16_splitk_workspace(int64_t m, int64_t n, int64_t k);
 

@@ -353,3 +353,11 @@ def test_splitk_noalloc_scratch_limit(lib):
     assert noalloc(lib, k=16384, lda=16384, ldb=16384, sbld=128) == -4
     assert lib.gemm_fp8_nt_bf16_splitk_workspace(64, 7168, 7168) <= 32 << 20
     assert noalloc(lib, m=0) == 0 and noalloc(lib, n=0) == 0
+
+
+def test_splitk_rejects_grids_beyond_32_bits(lib):
+    # n = 2^36 columns: 2^29 tiles of 128, whose fix-up grid (up to 4 workgroups a tile) would not fit 32 bits
+    n = 1 << 36
+    assert lib.gemm_fp8_nt_bf16_splitk_workspace(1, n, 128) == -1
+    assert splitk(lib, m=1, sald=4, n=n, k=128, lda=128, ldb=128, sbld=1, ldd=n) == -1
+    assert noalloc(lib, m=1, sald=4, n=n, k=128, lda=128, ldb=128, sbld=1, ldd=n) == -1
