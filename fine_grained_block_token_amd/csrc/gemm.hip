@@ -187,6 +187,17 @@ __device__ __forceinline__ void promote(v4f &acc, const v4f &p, const BlockScale
   for (int r = 0; r < 4; ++r) acc[r] = __builtin_fmaf(p[r], c, acc[r]);
 }
 
+// Round 4 fp32 values to bf16 (nearest, ties to even) and store them at dp (8-byte
+// aligned), only the first `left` when fewer than 4 columns remain.
+__device__ __forceinline__ void store_bf16x4(uint16_t *dp, const v4f &v, int64_t left) {
+  if (left >= 4) {
+    *reinterpret_cast<u32x2 *>(dp) =
+        (u32x2){bf16_rne(v[0]) | (bf16_rne(v[1]) << 16), bf16_rne(v[2]) | (bf16_rne(v[3]) << 16)};
+  } else {
+    for (int r = 0; r < left; ++r) dp[r] = (uint16_t)bf16_rne(v[r]);
+  }
+}
+
 // Tile of workgroup blockIdx.x: block b runs on XCD b % 8, each XCD takes a
 // contiguous range of tile ids, walked in bands of kGroupM m-tiles, so that the
 // tiles resident on one XCD share A and B panels in its L2.  False for the
@@ -499,6 +510,114 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_kernel(GemmAr
         for (int r = 0; r < 4; ++r)
           if (j + r < n) dp[r] = (uint16_t)bf16_rne(a[r]);
       }
+    }
+  }
+}
+
+// Few tiles and a long K (m = 512 decode: 224 or 128 tiles of 128x128 for 256 CUs):
+// there one workgroup's chain of K steps, about 0.85 us each whether a CU runs one
+// workgroup or two, sets the time.  Here a workgroup of 8 waves runs two chains on
+// one 128x128 tile: group g (waves 4g..4g+3, gemm_kernel's 2x2 wave layout) takes
+// K blocks g, g+2, g+4, ... through its own two LDS stages, with gemm_kernel's
+// copies, waits, fragment order and promotion; all 8 waves meet at each step's
+// barrier.  At the end group 1's promoted sums go through LDS and group 0 adds them
+// to its own (fixed order: the result is deterministic) and stores bf16.
+template <class C, int SA_FMT>
+__global__ __launch_bounds__(2 * C::kThreads, 1) void gemm_ksplit2_kernel(GemmArgs g, int tiles_m, int tiles_n) {
+  static_assert(C::kBM == 128 && C::kBN == 128 && C::kStages == 2, "128x128 tiles, two stages per group");
+  static_assert(2 * C::kStages * C::kStageBytes >= C::kWaves * 16 * 64 * 16, "the reduction fits the stages");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * C::kStages * C::kStageBytes];
+  const int t = threadIdx.x, lane = t & 63;
+  const int wg8 = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int grp = wg8 / C::kWaves, wv = wg8 % C::kWaves;
+  const int wm = (wv / C::WAVES_N_) * 64, wn = (wv % C::WAVES_N_) * 64;
+  int64_t m0, n0;
+  if (!tile_origin<C>(tiles_m, tiles_n, m0, n0)) return;
+  const int64_t m = g.m, n = g.n;
+  const int KB = (int)(g.k / kBK);
+  uint8_t *gs = smem + grp * C::kStages * C::kStageBytes;   // this group's two stages
+
+  const TileCopy<C> cp(g, m0, n0, wv, lane);
+  auto issue = [&](int kb, uint8_t *st) {
+    cp.tiles(g.A + m0 * g.lda + (int64_t)kb * kBK, g.B + n0 * g.ldb + (int64_t)kb * kBK, st, wv);
+    const int64_t col = SA_FMT == kSfPackedUe8m0 ? (kb >> 2) : kb;
+    cp.scales(reinterpret_cast<const uint32_t *>(g.sa) + col * g.sa_ld + m0, g.sb + (n0 >> 7) * g.sb_ld + kb, true,
+              st, wv);
+  };
+  auto read_scales = [&](int kb, const uint8_t *st, BlockScales &s) {
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+      const float v = *reinterpret_cast<const float *>(st + C::kSaOff + 4 * (wm + 16 * mi + (lane & 15)));
+      if constexpr (SA_FMT == kSfPackedUe8m0) {
+        s.sa[mi] = __uint_as_float(((__float_as_uint(v) >> (8 * (kb & 3))) & 0xFFu) << 23);
+      } else {
+        s.sa[mi] = v;
+      }
+    }
+    s.sb = *reinterpret_cast<const float *>(st + C::kSbOff);
+  };
+
+  BlockScales prev;
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi) prev.sa[mi] = 0.0f;
+  prev.sb = 0.0f;
+  v4f acc[16], p[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    acc[i] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+    p[i] = acc[i];
+  }
+
+  // step s: group g's block kb = 2s + g lives in its stage s%2; a group whose block
+  // is past K (group 1 in the last step of an odd KB) only meets the barrier
+  const int steps = (KB + 1) / 2;
+  if (grp < KB) issue(grp, gs);
+  for (int s = 0; s < steps; ++s) {
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier\n\ts_setprio 0" ::: "memory");
+    const int kb = 2 * s + grp;
+    if (kb >= KB) continue;   // wave-uniform
+    const uint8_t *st = gs + (s & 1) * C::kStageBytes;
+    if (kb + 2 < KB) issue(kb + 2, gs + ((s + 1) & 1) * C::kStageBytes);
+    BlockScales cur;
+    read_scales(kb, st, cur);
+    v8i af[4], bf[4];
+    af[0] = frag(st, wm + (lane & 15), lane);
+    bf[0] = frag(st + C::kABytes, wn + (lane & 15), lane);
+    bf[1] = frag(st + C::kABytes, wn + 16 + (lane & 15), lane);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      if (q < 2) bf[q + 2] = frag(st + C::kABytes, wn + 16 * (q + 2) + (lane & 15), lane);
+      else if (q < 5) af[q - 1] = frag(st, wm + 16 * (q - 1) + (lane & 15), lane);
+      const int mi = q >> 2, ni = (mi & 1) ? 3 - (q & 3) : (q & 3), i = 4 * mi + ni;
+      promote(acc[i], p[i], prev, mi);
+      p[i] = mfma_k128(bf[ni], af[mi]);
+      if (q == 0) __builtin_amdgcn_s_setprio(3);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    prev = cur;
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) promote(acc[i], p[i], prev, i >> 2);
+
+  // group 1 -> LDS (every stage read is done once all waves pass this barrier)
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  v4f *red = reinterpret_cast<v4f *>(smem) + wv * 16 * 64 + lane;
+  if (grp == 1) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) red[i * 64] = acc[i];
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  if (grp == 1) return;
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi) {
+    const int64_t i = m0 + wm + 16 * mi + (lane & 15);
+    if (i >= m) continue;
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) {
+      const int64_t j = n0 + wn + 16 * ni + 4 * (lane >> 4);
+      if (j >= n) continue;
+      const v4f a = acc[4 * mi + ni] + red[(4 * mi + ni) * 64];
+      store_bf16x4(reinterpret_cast<uint16_t *>(g.D) + i * g.ldd + j, a, n - j);
     }
   }
 }
@@ -951,17 +1070,6 @@ __global__ __launch_bounds__(64 * W) void gemm_skinny_kernel(GemmArgs g, int til
   }
 }
 
-// Round 4 fp32 values to bf16 (nearest, ties to even) and store them at dp (8-byte
-// aligned), only the first `left` when fewer than 4 columns remain.
-__device__ __forceinline__ void store_bf16x4(uint16_t *dp, const v4f &v, int64_t left) {
-  if (left >= 4) {
-    *reinterpret_cast<u32x2 *>(dp) =
-        (u32x2){bf16_rne(v[0]) | (bf16_rne(v[1]) << 16), bf16_rne(v[2]) | (bf16_rne(v[3]) << 16)};
-  } else {
-    for (int r = 0; r < left; ++r) dp[r] = (uint16_t)bf16_rne(v[r]);
-  }
-}
-
 // Wait until at most n (0 <= n < 32) vector memory operations of this wave are
 // outstanding, then meet the other waves at the barrier.  The count must be an
 // immediate: with n known at compile time (an unrolled loop) the chain folds to one
@@ -1238,6 +1346,18 @@ hipError_t launch_gemm_g32(const GemmArgs &args, hipStream_t st) {
   return hipGetLastError();
 }
 
+static hipError_t launch_ksplit2(const GemmArgs &a, hipStream_t st) {
+  using C = Cfg<2, 2, 2>;
+  const int tiles_m = (int)((a.m + C::kBM - 1) / C::kBM), tiles_n = (int)((a.n + C::kBN - 1) / C::kBN);
+  const int per_xcd = (tiles_m * tiles_n + kXcds - 1) / kXcds;
+  const dim3 grid((unsigned)(per_xcd * kXcds));
+  if (a.sa_fmt == kSfPackedUe8m0)
+    hipLaunchKernelGGL((gemm_ksplit2_kernel<C, kSfPackedUe8m0>), grid, dim3(2 * C::kThreads), 0, st, a, tiles_m, tiles_n);
+  else
+    hipLaunchKernelGGL((gemm_ksplit2_kernel<C, kSfFp32>), grid, dim3(2 * C::kThreads), 0, st, a, tiles_m, tiles_n);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm(const GemmArgs &a, hipStream_t st) {
   if (!a.wgrad && a.m_idx == nullptr && a.q == nullptr && a.m <= 64) {
     // decode-sized: stream B with K split over the waves of a workgroup
@@ -1251,6 +1371,10 @@ hipError_t launch_gemm(const GemmArgs &a, hipStream_t st) {
     if (a.m <= 32) return launch_skinny<2, 2, 8, 2>(a, st);
     return launch_skinny<4, 2, 8, 2>(a, st);
   }
+  // Fewer 128x128 tiles than CUs and a long K (m = 512 decode): two K chains per tile
+  if (!a.wgrad && a.m_idx == nullptr && a.q == nullptr && a.k >= 8 * kBK &&
+      ((a.m + 127) / 128) * ((a.n + 127) / 128) < cu_count())
+    return launch_ksplit2(a, st);
   // 128x128 output tiles, 4 waves, 2 LDS stages (66 KB): two workgroups per CU, so
   // one workgroup's barrier and copy latency is covered by the other's MFMAs.
   return launch_cfg<Cfg<2, 2, 2>>(a, st);

@@ -140,6 +140,39 @@ def test_gemm_decode(gpu, m, nk):
         check_bf16_gemm(got[ii, jj], ref, absum, tb, k // 128, f"decode {(m, n, k)}")
 
 
+@pytest.mark.parametrize("mnk", [(512, 7168, 1024), (300, 700, 1152), (129, 130, 2176), (384, 1000, 4096)])
+@pytest.mark.parametrize("fmt", [oracle.SF_FP32, oracle.SF_PACKED_UE8M0], ids=["fp32", "packed"])
+def test_gemm_two_k_chains(gpu, mnk, fmt):
+    # fewer 128x128 tiles than CUs and at least 8 K blocks: two groups of waves take the
+    # even and the odd K blocks of each tile and add their sums at the end; 9 and 17 K
+    # blocks leave the second group one step without a block
+    m, n, k = mnk
+    qa, sa, qb, sb = _cast_operands(m, n, k, scale=0.1, a_fmt=fmt)
+    sa_f = oracle.unpack_ue8m0(sa, k // 128) if fmt == oracle.SF_PACKED_UE8M0 else sa
+    got = _run_gemm(qa, sa, qb, sb, sa_fmt=fg.SF_PACKED_UE8M0 if fmt == oracle.SF_PACKED_UE8M0 else fg.SF_FP32)
+    ref, absum = oracle.gemm_nt(qa, sa_f, qb, sb)
+    check_bf16_gemm(got, ref, absum, mfma_truncation_bound(qa, sa_f, qb, sb), k // 128, f"two K chains {mnk} fmt {fmt}")
+
+
+def test_gemm_two_k_chains_one_hot(gpu):
+    # one nonzero K position per row, in an odd or an even K block: each output is one
+    # product a*b*sa*sb (exact in bf16), so a block summed by the wrong group, twice or
+    # not at all, or a wrong scale, shows as a wrong value
+    m, n, k = 200, 300, 1152
+    KB = k // 128
+    rng = np.random.default_rng(11)
+    qa = np.zeros((m, k), np.uint8)
+    pos = rng.integers(0, k, m)
+    qa[np.arange(m), pos] = 0x38  # 1.0
+    qb = np.full((n, k), 0x40, np.uint8)  # 2.0
+    sa = np.ldexp(1.0, rng.integers(-4, 5, (m, KB))).astype(np.float32)
+    sb = np.ldexp(1.0, rng.integers(-4, 5, (-(-n // 128), KB))).astype(np.float32)
+    got = _run_gemm(qa, sa, qb, sb)
+    want = 2.0 * sa[np.arange(m), pos // 128][:, None] * sb[np.arange(n) // 128][:, pos // 128].T
+    want_bits = (want.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    assert np.array_equal(got, want_bits)
+
+
 @pytest.mark.parametrize("m", [1, 5, 16, 17, 32, 33, 63, 64, 65])
 @pytest.mark.parametrize("nk", [(1000, 128), (200, 1152), (4096, 2176), (9000, 256), (7168, 1408)])
 def test_gemm_skinny_edges(gpu, m, nk):
