@@ -112,6 +112,17 @@ def test_gemm_one_hot_scale_indexing(gpu):
     assert np.array_equal(got, want)
 
 
+
+@pytest.mark.parametrize("mnk", [(1, 1, 128), (5, 1, 128), (64, 3, 1152), (130, 7, 256), (300, 17, 384),
+                                 (256, 9, 1152)])
+def test_gemm_tiny_n(gpu, mnk):
+    # fewer columns than one 16-wide MFMA tile: the decode kernel (m <= 64), the 128x128
+    # kernel and the two-K-chain kernel (2 tiles, 9 K blocks) with every B row past n clamped
+    qa, sa, qb, sb = _cast_operands(*mnk)
+    got = _run_gemm(qa, sa, qb, sb)
+    ref, absum = oracle.gemm_nt(qa, sa, qb, sb)
+    check_bf16_gemm(got, ref, absum, mfma_truncation_bound(qa, sa, qb, sb), mnk[2] // 128, f"gemm tiny n {mnk}")
+
 @pytest.mark.parametrize("mnk", [(4096, 7168, 7168), (4096, 4096, 7168)])
 def test_gemm_prefill_sampled(gpu, mnk):
     m, n, k = mnk
@@ -286,6 +297,18 @@ def test_wgrad_full_compare(gpu, shape):
     ref, absum = oracle.wgrad_nt(qa, sa, qb, sb, d_in_np)
     check_wgrad(got, ref, absum, -(-tokens // 128), f"wgrad {shape}")
 
+
+
+@pytest.mark.parametrize("shape", [(128, 1, 1), (256, 3, 130), (384, 130, 5)])
+def test_wgrad_tiny(gpu, shape):
+    # one output, a 3-row gradient over 130 columns, and 5 columns over 130 rows:
+    # partial 4-column groups and rows past m or n clamped in the copies
+    tokens, d_out, d_in = shape
+    qa, sa, qb, sb = _wgrad_operands(tokens, d_out, d_in)
+    d_in_np = si.randn((d_out, d_in), 7, 0.1, torch.float32).numpy()
+    got = _run_wgrad(qa, sa, qb, sb, d_in_np)
+    ref, absum = oracle.wgrad_nt(qa, sa, qb, sb, d_in_np)
+    check_wgrad(got, ref, absum, -(-tokens // 128), f"wgrad tiny {shape}")
 
 def test_wgrad_many_ragged_tiles(gpu):
     # d_out x d_in = 250 x 38360: 600 ragged tiles, 3 K blocks
