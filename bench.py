@@ -57,86 +57,65 @@ def parse():
 
 
 class Linear:
-    """Preallocated device buffers of one FP8 linear step."""
+    """The FP8 linear step on synthetic inputs: fine_grained_block_token_amd.linear.Fp8Linear
+    for each recipe, with the bench's op names."""
 
     def __init__(self, fg, torch, si, tokens, d_in, d_out):
+        from fine_grained_block_token_amd.linear import Fp8Linear
         dev = "cuda"
-        self.fg, self.torch = fg, torch
+        self.fg, self.torch, self._cls = fg, torch, Fp8Linear
         self.T, self.I, self.O = tokens, d_in, d_out
         self.x = si.randn((tokens, d_in), si.SEED_A).to(dev)
         self.W = si.randn((d_out, d_in), si.SEED_B).to(dev)
         self.dY = si.randn((tokens, d_out), si.SEED_DY).to(dev)
-        u8, f32 = torch.uint8, torch.float32
-        mk = lambda r, c: torch.empty((r, c), dtype=u8, device=dev)
-        self.xq, self.sx = mk(tokens, d_in), fg.mn_major_scales(tokens, d_in // 128)
-        self.Wq, self.sW = mk(d_out, d_in), torch.empty((d_out // 128, d_in // 128), dtype=f32, device=dev)
-        self.WqT, self.sWT = mk(d_in, d_out), torch.empty((d_in // 128, d_out // 128), dtype=f32, device=dev)
-        self.dYq, self.sdY = mk(tokens, d_out), fg.mn_major_scales(tokens, d_out // 128)
-        self.dYTq, self.sdYT = mk(d_out, tokens), fg.mn_major_scales(d_out, tokens // 128)
-        self.xTq, self.sxT = mk(d_in, tokens), fg.mn_major_scales(d_in, tokens // 128)
-        self.y = torch.empty((tokens, d_out), dtype=torch.bfloat16, device=dev)
-        self.dX = torch.empty((tokens, d_in), dtype=torch.bfloat16, device=dev)
-        self.dW = torch.zeros((d_out, d_in), dtype=f32, device=dev)
+        self.step = Fp8Linear(tokens, d_in, d_out, "fp32", dev)
+        self._ue8m0 = self._g32 = None
+
+    def __getattr__(self, name):
+        # the fp32-scale step's buffers (xq, sx, Wq, sW, y, ...) read as attributes
+        step = self.__dict__.get("step")
+        if step is None:
+            raise AttributeError(name)
+        return getattr(step, name)
+
+    @staticmethod
+    def _named(ops, names):
+        return [(n, fn) for n, (_, fn) in zip(names, ops)]
 
     def ops(self):
         """The step: x and dY are each read once by the dual-orientation cast, which emits
         both the row-wise operand (forward / dgrad) and the transposed one (wgrad)."""
-        fg = self.fg
-        return [
-            ("cast_x_dual", lambda: fg.cast_per_token_dual(self.x, self.xq, self.sx, self.xTq, self.sxT)),
-            ("cast_W", lambda: fg.cast_per_block(self.W, self.Wq, self.sW, self.WqT, self.sWT, fg.SF_FP32)),
-            ("gemm_fwd", lambda: fg.gemm_fp8_nt_bf16(self.xq, self.sx, self.Wq, self.sW, self.y)),
-            ("cast_dY_dual", lambda: fg.cast_per_token_dual(self.dY, self.dYq, self.sdY, self.dYTq, self.sdYT)),
-            ("gemm_dgrad", lambda: fg.gemm_fp8_nt_bf16(self.dYq, self.sdY, self.WqT, self.sWT, self.dX)),
-            ("gemm_wgrad", lambda: fg.wgrad_gemm_fp8_nt_fp32(self.dYTq, self.sdYT, self.xTq, self.sxT, self.dW)),
-        ]
+        return self._named(self.step.ops(self.x, self.W, self.dY),
+                           ["cast_x_dual", "cast_W", "gemm_fwd", "cast_dY_dual", "gemm_dgrad", "gemm_wgrad"])
 
     def separate_cast_ops(self):
         """The same four per-token casts as separate single-orientation launches (for reference)."""
-        fg = self.fg
+        fg, L = self.fg, self.step
         return [
-            ("cast_x", lambda: fg.cast_per_token(self.x, self.xq, self.sx, 128, fg.SF_FP32)),
-            ("cast_xT", lambda: fg.cast_per_token(self.x.t(), self.xTq, self.sxT, 128, fg.SF_FP32)),
-            ("cast_dY", lambda: fg.cast_per_token(self.dY, self.dYq, self.sdY, 128, fg.SF_FP32)),
-            ("cast_dYT", lambda: fg.cast_per_token(self.dY.t(), self.dYTq, self.sdYT, 128, fg.SF_FP32)),
+            ("cast_x", lambda: fg.cast_per_token(self.x, L.xq, L.sx, 128, fg.SF_FP32)),
+            ("cast_xT", lambda: fg.cast_per_token(self.x.t(), L.xTq, L.sxT, 128, fg.SF_FP32)),
+            ("cast_dY", lambda: fg.cast_per_token(self.dY, L.dYq, L.sdY, 128, fg.SF_FP32)),
+            ("cast_dYT", lambda: fg.cast_per_token(self.dY.t(), L.dYTq, L.sdYT, 128, fg.SF_FP32)),
         ]
 
     def ue8m0_ops(self):
         """The same step with the casts' UE8M0 option (every scale a power of two, stored as
-        fp32): all three GEMMs apply the exponents on the scaled MFMA, without promotion.
-        Reuses the step's buffers."""
-        fg = self.fg
-        U = fg.SF_UE8M0
-        return [
-            ("cast_x_dual_ue8m0", lambda: fg.cast_per_token_dual(self.x, self.xq, self.sx, self.xTq, self.sxT, U)),
-            ("cast_W_ue8m0", lambda: fg.cast_per_block(self.W, self.Wq, self.sW, self.WqT, self.sWT, U)),
-            ("gemm_fwd_ue8m0", lambda: fg.gemm_fp8_nt_bf16_ue8m0(self.xq, self.sx, self.Wq, self.sW, self.y, U)),
-            ("cast_dY_dual_ue8m0", lambda: fg.cast_per_token_dual(self.dY, self.dYq, self.sdY, self.dYTq, self.sdYT, U)),
-            ("gemm_dgrad_ue8m0", lambda: fg.gemm_fp8_nt_bf16_ue8m0(self.dYq, self.sdY, self.WqT, self.sWT, self.dX,
-                                                                  U)),
-            ("gemm_wgrad_ue8m0", lambda: fg.wgrad_gemm_fp8_nt_fp32_ue8m0(self.dYTq, self.sdYT, self.xTq, self.sxT,
-                                                                        self.dW, U)),
-        ]
+        fp32): all three GEMMs apply the exponents on the scaled MFMA, without promotion."""
+        if self._ue8m0 is None:
+            self._ue8m0 = self._cls(self.T, self.I, self.O, "ue8m0")
+        return self._named(self._ue8m0.ops(self.x, self.W, self.dY),
+                           ["cast_x_dual_ue8m0", "cast_W_ue8m0", "gemm_fwd_ue8m0", "cast_dY_dual_ue8m0",
+                            "gemm_dgrad_ue8m0", "gemm_wgrad_ue8m0"])
 
     def g32_ops(self):
         """The same step in the UE8M0 group-32 recipe: x, W and dY each cast once in both
-        orientations with 32-wide groups and packed UE8M0 scales (x, xT; W, WT; dY, dYT), and
-        the three GEMMs on the scaled MFMA.  Reuses the FP8 buffers."""
-        fg, torch = self.fg, self.torch
-        T, I, O = self.T, self.I, self.O
-        w = lambda r, c: fg.mn_major_scales(r, c // 128, torch.int32)
-        self.wx, self.wxT, self.wW, self.wWT, self.wdY, self.wdYT = w(T, I), w(I, T), w(O, I), w(I, O), w(T, O), w(O, T)
-        P = fg.SF_PACKED_UE8M0
-        return [
-            ("cast_x_dual_g32", lambda: fg.cast_per_token_dual(self.x, self.xq, self.wx, self.xTq, self.wxT, P, 32)),
-            ("cast_W_dual_g32", lambda: fg.cast_per_token_dual(self.W, self.Wq, self.wW, self.WqT, self.wWT, P, 32)),
-            ("gemm_fwd_g32", lambda: fg.gemm_fp8_nt_bf16_ue8m0_g32(self.xq, self.wx, self.Wq, self.wW, self.y)),
-            ("cast_dY_dual_g32", lambda: fg.cast_per_token_dual(self.dY, self.dYq, self.wdY, self.dYTq, self.wdYT, P,
-                                                                 32)),
-            ("gemm_dgrad_g32", lambda: fg.gemm_fp8_nt_bf16_ue8m0_g32(self.dYq, self.wdY, self.WqT, self.wWT, self.dX)),
-            ("gemm_wgrad_g32", lambda: fg.wgrad_gemm_fp8_nt_fp32_ue8m0_g32(self.dYTq, self.wdYT, self.xTq, self.wxT,
-                                                                          self.dW)),
-        ]
+        orientations with 32-wide groups and packed UE8M0 scales, and the three GEMMs on the
+        scaled MFMA."""
+        if self._g32 is None:
+            self._g32 = self._cls(self.T, self.I, self.O, "ue8m0_g32")
+        return self._named(self._g32.ops(self.x, self.W, self.dY),
+                           ["cast_x_dual_g32", "cast_W_dual_g32", "gemm_fwd_g32", "cast_dY_dual_g32",
+                            "gemm_dgrad_g32", "gemm_wgrad_g32"])
 
     def work(self):
         """Algorithmic flops (GEMMs) and HBM bytes (casts: read input once, write q + scales once)."""

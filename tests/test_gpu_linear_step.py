@@ -1,7 +1,8 @@
 """End-to-end GPU parity of one FP8 nn.Linear step (tokens 8192, in 7168, out
-4096), composed exactly as the benchmark runs it ("[Help] Starter script for
-nn.Linear for fwd,bwd": forward x.W^T, dgrad dY.W, wgrad dY^T.x with the
-operands cast per token / per block; "DeepGEMM Essentials", Part 18):
+4096), run by fine_grained_block_token_amd.linear.Fp8Linear as the benchmark runs
+it ("[Help] Starter script for nn.Linear for fwd,bwd": forward x.W^T, dgrad dY.W,
+wgrad dY^T.x with the operands cast per token / per block; "DeepGEMM Essentials",
+Part 18):
 
   cast_per_token_dual(x)  -> xq, sx (1x128 along in) and xTq, sxT (along tokens)
   cast_per_block(W)       -> Wq, sW and the exact transpose WqT, sWT
@@ -23,8 +24,8 @@ import numpy as np
 import pytest
 import torch
 
-import bench
 import fine_grained_block_token_amd as fg
+from fine_grained_block_token_amd.linear import Fp8Linear
 import oracle
 import synth_inputs as si
 from gpu_util import check_bf16_gemm, check_wgrad, mfma_truncation_bound, sample_idx, say
@@ -42,11 +43,16 @@ def host_inputs():
     return si.host_array(x), si.host_array(W), si.host_array(dY)
 
 
-def _run(fg_, ops):
-    for name, fn in ops:
-        say("linear step", name)
+def _run(recipe):
+    x = si.randn((T, I), si.SEED_A).cuda()
+    W = si.randn((O, I), si.SEED_B).cuda()
+    dY = si.randn((T, O), si.SEED_DY).cuda()
+    L = Fp8Linear(T, I, O, recipe)
+    for name, fn in L.ops(x, W, dY):
+        say("linear step", recipe, name)
         fn()
     torch.cuda.synchronize()
+    return L
 
 
 def _u8(t):
@@ -69,8 +75,7 @@ def _bf16_bits(t):
 
 def test_linear_step_fp32_scales(gpu, host_inputs):
     xh, Wh, dYh = host_inputs
-    L = bench.Linear(fg, torch, si, T, I, O)
-    _run(fg, L.ops())
+    L = _run("fp32")
 
     # casts: bit-exact, both orientations
     qx, sx = oracle.cast_per_token(xh, 128, oracle.SF_FP32)
@@ -108,8 +113,7 @@ def test_linear_step_ue8m0_scales(gpu, host_inputs):
     # the same step with the casts' UE8M0 option: every scale a power of two, applied
     # by the scaled MFMA in all three GEMMs
     xh, Wh, dYh = host_inputs
-    L = bench.Linear(fg, torch, si, T, I, O)
-    _run(fg, L.ue8m0_ops())
+    L = _run("ue8m0")
     U = oracle.SF_UE8M0
     qx, sx = oracle.cast_per_token(xh, 128, U)
     qxT, sxT = oracle.cast_per_token(xh, 128, U, transpose=True)
@@ -138,12 +142,11 @@ def test_linear_step_g32_recipe(gpu, host_inputs):
     # the UE8M0 group-32 recipe: x, W and dY each cast once in both orientations with
     # 1x32 groups and packed scales; the three GEMMs on the scaled MFMA
     xh, Wh, dYh = host_inputs
-    L = bench.Linear(fg, torch, si, T, I, O)
-    _run(fg, L.g32_ops())
+    L = _run("ue8m0_g32")
     P = oracle.SF_PACKED_UE8M0
     casts = {}
-    for name, h, gq, gs, gqT, gsT in [("x", xh, L.xq, L.wx, L.xTq, L.wxT), ("W", Wh, L.Wq, L.wW, L.WqT, L.wWT),
-                                       ("dY", dYh, L.dYq, L.wdY, L.dYTq, L.wdYT)]:
+    for name, h, gq, gs, gqT, gsT in [("x", xh, L.xq, L.sx, L.xTq, L.sxT), ("W", Wh, L.Wq, L.sW, L.WqT, L.sWT),
+                                       ("dY", dYh, L.dYq, L.sdY, L.dYTq, L.sdYT)]:
         q, w = oracle.cast_per_token(h, 32, P)
         qT, wT = oracle.cast_per_token(h, 32, P, transpose=True)
         _same(gq, gs, q, w, f"g32 {name}")
