@@ -786,12 +786,13 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_g32_kernel(Ge
 // last one.  (bf16 rather than f16: the same sums, and the bf16 MFMA measured
 // 2-10% faster in this kernel on MI355X.)
 //
-// Cost, measured on MI355X: a conversion takes ~4 clocks per two values and a
-// VALU instruction overlaps an MFMA only for the first ~2 per MFMA, so with two
-// conversions and two promotion instructions per MFMA the fp32-scale kernel is
-// bound by the VALU: 458-490 us for 4096 x 7168 x 8192 (UE8M0 scales, no promotion:
-// 395-402 us), against 305-311 us for
-// the same pipeline on the FP8 MFMA.
+// Cost, measured on MI355X: with two waves per SIMD a conversion costs about as
+// much issue time as an FMA, and VALU instructions beyond the first one or two per
+// MFMA add their issue time to the MFMA's, so with two conversions and two
+// promotion instructions per 16x16x32 MFMA the fp32-scale kernel is bound by VALU
+// issue (MFMA busy ~46% of cycles): 430-490 us for 4096 x 7168 x 8192, 326 us with
+// the VALU work removed in a timing-only build; UE8M0 scales (no promotion)
+// 389-402 us; the same pipeline on the FP8 MFMA 305-311 us.
 typedef __bf16 b8 __attribute__((ext_vector_type(8)));
 
 // bf16 operand of slice s of 16 FP8 bytes, each value times the power of two
