@@ -167,3 +167,33 @@ def test_linear_step_g32_recipe(gpu, host_inputs):
     ii, jj = sample_idx(O, I, 20000, 39)
     ref, absum = oracle.wgrad_nt_g32(qdYT, sdYT, qxT, sxT, np.zeros((O, I), np.float32), idx=(ii, jj))
     check_wgrad(L.dW.cpu().numpy()[ii, jj], ref, absum, T // 32, "linear step g32 wgrad")
+
+
+@pytest.mark.parametrize("recipe", ["fp32", "ue8m0", "ue8m0_g32"])
+def test_linear_step_graph_replay(gpu, recipe):
+    # the whole step captured in one HIP graph (as the benchmark times it): every replay
+    # gives the eager step's y and dX bit for bit, and dW accumulates exactly as the same
+    # number of eager steps does
+    t, i, o = 512, 384, 256
+    x = si.randn((t, i), si.SEED_A).cuda()
+    W = si.randn((o, i), si.SEED_B).cuda()
+    dY = si.randn((t, o), si.SEED_DY).cuda()
+    eager, graphed = Fp8Linear(t, i, o, recipe), Fp8Linear(t, i, o, recipe)
+    say("linear step graph", recipe, (t, i, o))
+    graphed.step(x, W, dY)                      # warm (and the first accumulation into dW)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            graphed.step(x, W, dY)
+    torch.cuda.current_stream().wait_stream(s)
+    eager.step(x, W, dY)
+    for r in range(3):
+        g.replay()
+        eager.step(x, W, dY)
+        torch.cuda.synchronize()
+        assert torch.equal(graphed.y.view(torch.int16), eager.y.view(torch.int16)), f"y differs on replay {r}"
+        assert torch.equal(graphed.dX.view(torch.int16), eager.dX.view(torch.int16)), f"dX differs on replay {r}"
+        assert torch.equal(graphed.dW, eager.dW), f"dW differs after replay {r}"
