@@ -139,25 +139,28 @@ class Linear:
 
 
 def timed_ops(torch, ops, steps, warmup):
+    """Warm-up steps, then `steps` eager steps with one HIP event between consecutive kernels
+    (each kernel's time is the interval between the events around it, so the intervals add
+    up to the timed region); returns the total and the mean time of each op."""
     for _ in range(warmup):
         for _, fn in ops:
             fn()
     torch.cuda.synchronize()
-    ev = {name: [] for name, _ in ops}
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps * len(ops) + 1)]
     torch.cuda.synchronize()
-    start.record()
+    evs[0].record()
+    j = 0
     for _ in range(steps):
-        for name, fn in ops:
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
+        for _, fn in ops:
             fn()
-            b.record()
-            ev[name].append((a, b))
-    end.record()
+            j += 1
+            evs[j].record()
     torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
-    per = {name: sum(a.elapsed_time(b) for a, b in pairs) / len(pairs) for name, pairs in ev.items()}
+    total_ms = evs[0].elapsed_time(evs[-1])
+    per = {name: 0.0 for name, _ in ops}
+    for j in range(steps * len(ops)):
+        per[ops[j % len(ops)][0]] += evs[j].elapsed_time(evs[j + 1])
+    per = {name: v / steps for name, v in per.items()}
     return total_ms, per
 
 
