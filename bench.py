@@ -316,8 +316,9 @@ def extra_kernels(fg, torch, si):
         r["gbs"] = nbytes / (r["ms"] * 1e-3) / 1e9
         r["frac_hbm_peak"] = r["gbs"] / PEAK_HBM_GBS
         out[f"gemm_{m}x{n}x{k}"] = r
-        if m <= 64:
-            # the stream-K decode GEMM (K split evenly over the CUs) on the same operands
+        if fg.gemm_fp8_nt_bf16_splitk_workspace(m, n, k) > 0:
+            # the split-K GEMM on the same operands (m <= 64: stream-K shares evenly over
+            # the CUs; m = 512: each 128x128 tile's K in 2 or 4 slices)
             ws = torch.empty((fg.gemm_fp8_nt_bf16_splitk_workspace(m, n, k) // 4,), dtype=torch.float32,
                              device="cuda")
             r = _measure(torch, "TFLOPS", 2.0 * m * n * k,

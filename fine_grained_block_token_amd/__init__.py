@@ -179,7 +179,7 @@ def gemm_fp8_nt_bf16(A: torch.Tensor, sa: torch.Tensor, B: torch.Tensor, sb: tor
 
 
 def gemm_fp8_nt_bf16_splitk_workspace(m: int, n: int, k: int) -> int:
-    """Bytes of workspace gemm_fp8_nt_bf16_splitk needs for an [m, k] x [n, k]^T product (m <= 64)."""
+    """Bytes of workspace gemm_fp8_nt_bf16_splitk needs for an [m, k] x [n, k]^T product (0: none)."""
     r = load().gemm_fp8_nt_bf16_splitk_workspace(m, n, k)
     if r < 0:
         raise Fgfp8Error(f"gemm_fp8_nt_bf16_splitk_workspace: {load().fgfp8_status_string(int(r)).decode()}")
@@ -188,8 +188,9 @@ def gemm_fp8_nt_bf16_splitk_workspace(m: int, n: int, k: int) -> int:
 
 def gemm_fp8_nt_bf16_splitk(A: torch.Tensor, sa: torch.Tensor, B: torch.Tensor, sb: torch.Tensor, D: torch.Tensor,
                             workspace: torch.Tensor, sa_fmt: int = SF_FP32) -> None:
-    """gemm_fp8_nt_bf16 for m <= 64 with K split over workgroups; ``workspace`` is a device tensor of
-    at least gemm_fp8_nt_bf16_splitk_workspace(m, n, k) bytes (any dtype, contents ignored)."""
+    """gemm_fp8_nt_bf16 with K split over workgroups (stream-K shares for m <= 64, K slices of
+    128x128 tiles above); ``workspace`` is a device tensor of at least
+    gemm_fp8_nt_bf16_splitk_workspace(m, n, k) bytes (any dtype, contents ignored)."""
     A, B = _u8(A), _u8(B)
     m, k = A.shape
     n = B.shape[0]

@@ -180,10 +180,18 @@ int gemm_fp8_nt_bf16(const uint8_t *A, int64_t lda, const void *sa, int sa_fmt, 
   return launched(fgfp8::launch_gemm(a, static_cast<hipStream_t>(stream)));
 }
 
+// Limits of the split-K plans: stream-K (m <= 64) indexes units in 32 bits and runs
+// up to 4 fix-up workgroups per 128-column tile; K slices (m > 64) share
+// gemm_fp8_nt_bf16's tile-count limit.
+static bool splitk_fits(int64_t m, int64_t n, int64_t k) {
+  if (m > 64) return cdiv(m, 128) <= 0x7FFFFFFF && cdiv(n, 128) <= 0x7FFFFFFF;
+  return cdiv(n, 128) * (k / 128) <= 0x7FFFFFF0 && cdiv(n, 128) <= 0x1FFFFFFF;
+}
+
 int64_t gemm_fp8_nt_bf16_splitk_workspace(int64_t m, int64_t n, int64_t k) {
-  if (m < 0 || m > 64 || n < 0 || k <= 0 || k % 128 != 0) return FGFP8_EINVAL;
+  if (m < 0 || n < 0 || k <= 0 || k % 128 != 0) return FGFP8_EINVAL;
   if (m == 0 || n == 0) return 0;
-  if (cdiv(n, 128) * (k / 128) > 0x7FFFFFF0 || cdiv(n, 128) > 0x1FFFFFFF) return FGFP8_EINVAL;
+  if (!splitk_fits(m, n, k)) return FGFP8_EINVAL;
   return fgfp8::splitk_plan(m, n, k).workspace_bytes;
 }
 
@@ -192,15 +200,14 @@ int gemm_fp8_nt_bf16_splitk(const uint8_t *A, int64_t lda, const void *sa, int s
                             int64_t m, int64_t n, int64_t k, void *workspace, int64_t workspace_bytes,
                             void *stream) {
   if (sa_fmt != kSfFp32 && sa_fmt != kSfUe8m0 && sa_fmt != kSfPackedUe8m0) return FGFP8_EINVAL;
-  if (m > 64) return FGFP8_EINVAL;
   const int c = check_gemm_common(A, lda, sa, sa_ld, B, ldb, sb, D, m, n, k);
   if (c != 1) return c;
   if (sb_ld < k / 128) return FGFP8_EINVAL;
   if (!aligned(D, 16) || ldd < n || ldd % 8 != 0) return FGFP8_EINVAL;
-  // unit indices are 32-bit, and so is the fix-up grid (up to 4 workgroups per 128-column tile)
-  if (cdiv(n, 128) * (k / 128) > 0x7FFFFFF0 || cdiv(n, 128) > 0x1FFFFFFF) return FGFP8_EINVAL;
+  if (!splitk_fits(m, n, k)) return FGFP8_EINVAL;
   const fgfp8::SplitKPlan plan = fgfp8::splitk_plan(m, n, k);
-  if (!workspace || !aligned(workspace, 16) || workspace_bytes < plan.workspace_bytes) return FGFP8_EINVAL;
+  if (plan.workspace_bytes > 0 && (!workspace || !aligned(workspace, 16) || workspace_bytes < plan.workspace_bytes))
+    return FGFP8_EINVAL;
   const int dev = check_device();
   if (dev != FGFP8_OK) return dev;
   fgfp8::GemmArgs a{A, lda, sa, sa_fmt, sa_ld, B, ldb, sb, sb_ld, D, ldd, m, n, k, false};
@@ -211,12 +218,11 @@ int gemm_fp8_nt_bf16_splitk_noalloc(const uint8_t *A, int64_t lda, const void *s
                                     const uint8_t *B, int64_t ldb, const float *sb, int64_t sb_ld, uint16_t *D,
                                     int64_t ldd, int64_t m, int64_t n, int64_t k, void *stream) {
   if (sa_fmt != kSfFp32 && sa_fmt != kSfUe8m0 && sa_fmt != kSfPackedUe8m0) return FGFP8_EINVAL;
-  if (m > 64) return FGFP8_EINVAL;
   const int c = check_gemm_common(A, lda, sa, sa_ld, B, ldb, sb, D, m, n, k);
   if (c != 1) return c;
   if (sb_ld < k / 128) return FGFP8_EINVAL;
   if (!aligned(D, 16) || ldd < n || ldd % 8 != 0) return FGFP8_EINVAL;
-  if (cdiv(n, 128) * (k / 128) > 0x7FFFFFF0 || cdiv(n, 128) > 0x1FFFFFFF) return FGFP8_EINVAL;
+  if (!splitk_fits(m, n, k)) return FGFP8_EINVAL;
   const fgfp8::SplitKPlan plan = fgfp8::splitk_plan(m, n, k);
   if (plan.workspace_bytes > FGFP8_SCRATCH_BYTES) return FGFP8_ESCRATCH;
   const int dev = check_device();

@@ -352,8 +352,12 @@ __device__ __forceinline__ void fused_cast_epilogue(const GemmArgs &g, const v4f
   }
 }
 
-template <class C, int SA_FMT, bool GROUPED, int CASTF>
+// KSLICE: the workgroup takes K blocks [KB*y/Y, KB*(y+1)/Y) of its tile, y =
+// blockIdx.y of Y = gridDim.y slices (the launcher keeps Y <= KB, so no slice is
+// empty), and stores its promoted fp32 sums to the workspace instead of D.
+template <class C, int SA_FMT, bool GROUPED, int CASTF, bool KSLICE = false>
 __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_kernel(GemmArgs g, int tiles_m, int tiles_n) {
+  static_assert(!KSLICE || (!GROUPED && CASTF == 0), "K slices of plain tiles only");
   // the stages, then a 1 KB slot that receives the B prefetch copies
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::kStages * C::kStageBytes + 1024];
   const int t = threadIdx.x, lane = t & 63;
@@ -363,6 +367,12 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_kernel(GemmAr
   if (!tile_origin<C>(tiles_m, tiles_n, m0, n0)) return;
   const int64_t m = g.m, n = g.n;
   const int KB = (int)(g.k / kBK);
+  int kb_lo = 0, kb_hi = KB;
+  if constexpr (KSLICE) {
+    kb_lo = (int)((int64_t)KB * blockIdx.y / gridDim.y);
+    kb_hi = (int)((int64_t)KB * (blockIdx.y + 1) / gridDim.y);
+    if (kb_lo >= kb_hi) return;   // not launched so; nothing issued yet
+  }
 
   // m-grouped layout: the tile's 128 rows belong to one expert, the largest
   // m_indices among them (-1 marks padding); a tile with no valid expert id
@@ -441,10 +451,10 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_kernel(GemmAr
   // (20 steps back to back): dgrad 291 -> 273 us (its B, W^T, was written long
   // before), forward +1%, step -1.4%.  The launcher enables it for grids of more
   // than one round only.
-  issue(0, smem);
-  const bool prefetching = !GROUPED && (int)blockIdx.x < g.b_prefetch_wgs;
+  issue(kb_lo, smem + (kb_lo & 1) * C::kStageBytes);
+  const bool prefetching = !GROUPED && !KSLICE && (int)blockIdx.x < g.b_prefetch_wgs;
   if (prefetching) b_prefetch<C>(g, n, wv, lane, smem + C::kStages * C::kStageBytes);
-  for (int kb = 0; kb < KB; ++kb) {
+  for (int kb = kb_lo; kb < kb_hi; ++kb) {
     // wave priority 0 while waiting and issuing copies, 3 once its MFMAs run (below):
     // the SIMD's other wave, if it is in its MFMA phase, is served first
     if (prefetching && kb == 0)   // block 0 has landed; the prefetch copies may be in flight
@@ -454,7 +464,7 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_kernel(GemmAr
     const uint8_t *st = smem + (kb & 1) * C::kStageBytes;
     // The copy into the free stage goes first: inline assembly bounds the
     // scheduling region, and the fragment reads must share one with the MFMAs.
-    if (kb + 1 < KB) issue(kb + 1, smem + ((kb + 1) & 1) * C::kStageBytes);
+    if (kb + 1 < kb_hi) issue(kb + 1, smem + ((kb + 1) & 1) * C::kStageBytes);
     BlockScales cur;
     read_scales(kb, st, cur);
     // Tiles run in a snake order (row 0 left to right, row 1 right to left, ...)
@@ -482,6 +492,15 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_kernel(GemmAr
   }
 #pragma unroll
   for (int i = 0; i < 16; ++i) promote(acc[i], p[i], prev, i >> 2);
+
+  if constexpr (KSLICE) {
+    // slot (tile, slice): per wave 16 x 64 lanes of v4f, each store 1 KB contiguous
+    const int64_t tile = (m0 / C::kBM) * tiles_n + n0 / C::kBN;
+    v4f *dst = reinterpret_cast<v4f *>(g.part) + ((tile * gridDim.y + blockIdx.y) * C::kWaves + wv) * 1024 + lane;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dst[i * 64] = acc[i];
+    return;
+  }
 
   // epilogue: lane holds row i, columns j..j+3 of every 16x16 tile
   if constexpr (CASTF != 0) fused_cast_epilogue<C, CASTF == 2>(g, acc, m0, n0, wm, wn, lane);
@@ -1248,6 +1267,31 @@ __global__ __launch_bounds__(512) void streamk_fixup_kernel(GemmArgs g, const fl
   store_bf16x4(reinterpret_cast<uint16_t *>(g.D) + row * g.ldd + col, sum, g.n - col);
 }
 
+// K-sliced 128x128 tiles: D = bf16 of the sum of the tile's S slot partials, added in
+// slice order (deterministic).  One workgroup per (tile, wave quarter of the tile):
+// thread t takes v4f positions t, t + 256, t + 512, t + 768 of that wave's 16 x 64
+// lanes, with all S loads of a position issued before the adds.
+template <class C, int S>
+__global__ __launch_bounds__(256) void kslice_fixup_kernel(GemmArgs g, int tiles_n) {
+  static_assert(C::kWaves == 4, "four 64x64 wave blocks per tile");
+  const int tile = (int)blockIdx.x >> 2, wv = (int)blockIdx.x & 3;
+  const int64_t m0 = (int64_t)(tile / tiles_n) * C::kBM, n0 = (int64_t)(tile % tiles_n) * C::kBN;
+  const int wm = (wv / C::WAVES_N_) * 64, wn = (wv % C::WAVES_N_) * 64;
+  const v4f *src = reinterpret_cast<const v4f *>(g.part) + ((int64_t)tile * S * C::kWaves + wv) * 1024;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int pos = r * 256 + (int)threadIdx.x, i = pos >> 6, lane = pos & 63;
+    v4f v[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) v[s] = src[(int64_t)s * C::kWaves * 1024 + pos];
+    v4f sum = v[0];
+#pragma unroll
+    for (int s = 1; s < S; ++s) sum += v[s];
+    const int64_t row = m0 + wm + 16 * (i >> 2) + (lane & 15), col = n0 + wn + 16 * (i & 3) + 4 * (lane >> 4);
+    if (row < g.m && col < g.n) store_bf16x4(reinterpret_cast<uint16_t *>(g.D) + row * g.ldd + col, sum, g.n - col);
+  }
+}
+
 }  // namespace
 
 // Compute units of the current device (queried once per device).
@@ -1381,12 +1425,37 @@ hipError_t launch_gemm(const GemmArgs &a, hipStream_t st) {
   return launch_cfg<Cfg<2, 2, 2>>(a, st);
 }
 
-// Stream-K plan for m <= 64: units = 128-column tiles x K blocks; UPW units per
+constexpr int64_t kMaxSlices = 4;
+
+// Split-K plans.  m > 64: 128x128 tiles, K cut into S slices, for at most 128 tiles
+// (half the CUs of the 256-CU part: with more, the plain kernels already fill the
+// part and the slices' extra pass over the partial sums loses).  S is the largest
+// of 2..4 with at least 8 K blocks per slice, and at least 12 once tiles * S
+// passes one workgroup per CU; S = 1 (the plain kernel, no workspace) when none
+// qualifies.  Measured on MI355X (B streamed from HBM), plain -> sliced: 512 x
+// 4096 x 7168 41 -> 33 us (S = 4), 128 x 4096 x 7168 41 -> 20 us, 256 x 7168 x
+// 4096 26 -> 23 us (S = 2, where S = 4 took 26 us).  m <= 64 (stream-K): units = 128-column tiles x K blocks; UPW units per
 // workgroup, the fewest (at most 8) that keep the workgroups within one per CU of
 // the 256-CU part (more than 256 only when that takes over 8 units each).
 SplitKPlan splitk_plan(int64_t m, int64_t n, int64_t k) {
   SplitKPlan p;
   p.tiles_n = (n + 127) / 128;
+  if (m > 64) {
+    p.tiles_m = (m + 127) / 128;
+    const int64_t tiles = p.tiles_m * p.tiles_n;
+    const int64_t kb = k / kBK;
+    p.slices = 1;
+    if (tiles <= kStreamKSlots / 2)
+      for (int64_t s = kMaxSlices; s >= 2; --s)
+        if (kb >= 8 * s && (tiles * s <= kStreamKSlots || kb >= 12 * s)) {
+          p.slices = s;
+          break;
+        }
+    p.units = p.upw = 0;
+    p.grid = tiles * p.slices;
+    p.workspace_bytes = p.slices > 1 ? tiles * p.slices * 128 * 128 * (int64_t)sizeof(float) : 0;
+    return p;
+  }
   p.units = p.tiles_n * (k / kBK);
   p.upw = std::min<int64_t>(8, std::max<int64_t>(1, (p.units + kStreamKSlots - 1) / kStreamKSlots));
   p.grid = (p.units + p.upw - 1) / p.upw;
@@ -1424,8 +1493,31 @@ static void launch_streamk_mt(const GemmArgs &a, float *part, const SplitKPlan &
                        (int)p.upw);
 }
 
+static hipError_t launch_kslice(const GemmArgs &args, float *part, const SplitKPlan &p, hipStream_t st) {
+  using C = Cfg<2, 2, 2>;
+  const int tiles_m = (int)p.tiles_m, tiles_n = (int)p.tiles_n;
+  const int per_xcd = (tiles_m * tiles_n + kXcds - 1) / kXcds;
+  const dim3 grid((unsigned)(per_xcd * kXcds), (unsigned)p.slices);
+  GemmArgs a = args;
+  a.part = part;
+  a.b_prefetch_wgs = 0;
+  if (a.sa_fmt == kSfPackedUe8m0)
+    hipLaunchKernelGGL((gemm_kernel<C, kSfPackedUe8m0, false, 0, true>), grid, dim3(C::kThreads), 0, st, a, tiles_m,
+                       tiles_n);
+  else
+    hipLaunchKernelGGL((gemm_kernel<C, kSfFp32, false, 0, true>), grid, dim3(C::kThreads), 0, st, a, tiles_m, tiles_n);
+  const dim3 fgrid((unsigned)(tiles_m * tiles_n * 4));
+  switch (p.slices) {
+    case 2: hipLaunchKernelGGL((kslice_fixup_kernel<C, 2>), fgrid, dim3(256), 0, st, a, tiles_n); break;
+    case 3: hipLaunchKernelGGL((kslice_fixup_kernel<C, 3>), fgrid, dim3(256), 0, st, a, tiles_n); break;
+    default: hipLaunchKernelGGL((kslice_fixup_kernel<C, 4>), fgrid, dim3(256), 0, st, a, tiles_n); break;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm_splitk(const GemmArgs &a, void *ws, const SplitKPlan &p, hipStream_t st) {
   float *part = static_cast<float *>(ws);
+  if (a.m > 64) return p.slices > 1 ? launch_kslice(a, part, p, st) : launch_gemm(a, st);
   if (a.m <= 16) launch_streamk_mt<1>(a, part, p, st);
   else if (a.m <= 32) launch_streamk_mt<2>(a, part, p, st);
   else launch_streamk_mt<4>(a, part, p, st);

@@ -91,6 +91,9 @@ struct GemmArgs {
   // Workgroups (blockIdx.x below this) that first read all of B through the
   // caches, so that later rounds of tiles find it in the MALL; 0: none.
   int b_prefetch_wgs = 0;
+  // K-sliced 128x128 tiles (split-K entry point, m > 64): the fp32 partial sums
+  // of slice s of tile t go to slot t*slices + s of part (64 KB each).
+  float *part = nullptr;
 };
 
 hipError_t launch_cast_per_token(const CastTokenArgs &a, hipStream_t st);
@@ -98,11 +101,15 @@ hipError_t launch_cast_per_block(const CastBlockArgs &a, hipStream_t st);
 hipError_t launch_cast_dual(const CastDualArgs &a, hipStream_t st);
 hipError_t launch_gemm(const GemmArgs &a, hipStream_t st);
 
-// Stream-K decode GEMM (m <= 64, bf16 output).  Workspace: 2*grid slots of
-// 16*ceil(m/16) x 128 fp32 partial sums.
+// Split-K GEMM (bf16 output).  m <= 64: stream-K over 128-column tiles x K blocks,
+// workspace 2*grid slots of 16*ceil(m/16) x 128 fp32 partial sums.  m > 64:
+// 128x128 tiles with K cut into `slices` consecutive ranges, one workgroup each,
+// workspace tiles*slices slots of 128x128 fp32 (slices == 1: the plain kernel,
+// no workspace).
 constexpr int64_t kStreamKSlots = 256;   // workgroups the plan aims at (one per CU)
 struct SplitKPlan {
   int64_t tiles_n, units, upw, grid, workspace_bytes;
+  int64_t tiles_m = 0, slices = 0;
 };
 SplitKPlan splitk_plan(int64_t m, int64_t n, int64_t k);
 hipError_t launch_gemm_splitk(const GemmArgs &a, void *ws, const SplitKPlan &p, hipStream_t st);

@@ -194,26 +194,36 @@ int gemm_fp8_nt_bf16(const uint8_t *A, int64_t lda, const void *sa, int sa_fmt, 
 
 /*
  * gemm_fp8_nt_bf16_splitk -- the same product as gemm_fp8_nt_bf16 (same
- * definition, passages and operand layouts), for decode-sized m <= 64, with
- * K split over workgroups ("DeepGEMM Essentials", Part 14: at these sizes the
- * product is bound by reading B once, so the work is spread evenly over the
- * compute units).  The K blocks of all 128-column tiles are dealt out in equal
- * consecutive shares, one per workgroup; a tile that a share covers whole is
- * rounded and stored at once, and a tile split between shares gets the fp32
- * promoted partial sums of its shares added in share order by a second kernel
- * (deterministic: the same inputs give the same bits on every call), then
- * rounded to bf16.  Each share's sum follows the definition above block by
- * block; only the grouping of the fp32 additions over K blocks differs from
+ * definition, passages and operand layouts) with K split over workgroups, for
+ * products with too few output tiles to fill the GPU ("DeepGEMM Essentials",
+ * Part 14: decode-sized products are bound by reading B once, so the work is
+ * spread evenly over the compute units).
+ *   m <= 64: the K blocks of all 128-column tiles are dealt out in equal
+ *     consecutive shares, one per workgroup; a tile that a share covers whole
+ *     is rounded and stored at once, and a tile split between shares gets the
+ *     fp32 promoted partial sums of its shares added in share order by a
+ *     second kernel, then rounded to bf16.
+ *   m > 64: with at most 128 output tiles of 128x128, each tile's K blocks
+ *     are cut into S consecutive slices, one workgroup per slice, and a second
+ *     kernel adds each tile's S fp32 partial sums in slice order and rounds to
+ *     bf16.  S is the largest of 2..4 with at least 8 K blocks per slice, and
+ *     at least 12 when tiles * S exceeds 256.  With more tiles, or when no
+ *     S >= 2 qualifies, the call runs gemm_fp8_nt_bf16's kernels and needs no
+ *     workspace.
+ * Deterministic: the same inputs give the same bits on every call.  Each
+ * share's or slice's sum follows the definition above block by block; only
+ * the grouping of the fp32 additions over K blocks differs from
  * gemm_fp8_nt_bf16, so the two agree to fp32 rounding, not bit for bit.
  *
  * workspace        device memory, 16-byte aligned, at least
  *                  gemm_fp8_nt_bf16_splitk_workspace(m, n, k) bytes, owned by
  *                  the caller; its contents on entry do not matter and are
- *                  overwritten.  Calls that share a workspace must be ordered
- *                  (one stream, or events): two in flight at once race.
- * m                0 <= m <= 64 (FGFP8_EINVAL above 64).
- * Other arguments, errors and k, n as gemm_fp8_nt_bf16; also FGFP8_EINVAL
- * when ceil(n/128) * k/128 exceeds 2^31 - 16 or ceil(n/128) exceeds 2^29 - 1.
+ *                  overwritten.  May be NULL when that size is 0.  Calls that
+ *                  share a workspace must be ordered (one stream, or events):
+ *                  two in flight at once race.
+ * Other arguments, errors and m, k, n as gemm_fp8_nt_bf16; also, for m <= 64,
+ * FGFP8_EINVAL when ceil(n/128) * k/128 exceeds 2^31 - 16 or ceil(n/128)
+ * exceeds 2^29 - 1.
  */
 int gemm_fp8_nt_bf16_splitk(const uint8_t *A, int64_t lda, const void *sa, int sa_fmt, int64_t sa_ld,
                             const uint8_t *B, int64_t ldb, const float *sb, int64_t sb_ld,
@@ -222,11 +232,13 @@ int gemm_fp8_nt_bf16_splitk(const uint8_t *A, int64_t lda, const void *sa, int s
 
 /*
  * gemm_fp8_nt_bf16_splitk_workspace -- bytes of workspace that
- * gemm_fp8_nt_bf16_splitk needs for (m, n, k): 2 * G * 16*ceil(m/16) * 128 * 4
- * (two partial-sum slots per workgroup), G the number of workgroups (which
- * depends on n and k only).  0 when m or n is 0; FGFP8_EINVAL (-1) when m is
- * outside 0..64, n < 0, k is not a positive multiple of 128, or the limits
- * of gemm_fp8_nt_bf16_splitk on n and k are exceeded.  Host only: launches
+ * gemm_fp8_nt_bf16_splitk needs for (m, n, k).  m <= 64:
+ * 2 * G * 16*ceil(m/16) * 128 * 4 (two partial-sum slots per workgroup), G the
+ * number of workgroups (which depends on n and k only).  m > 64:
+ * ceil(m/128) * ceil(n/128) * S * 128 * 128 * 4 (one slot per tile and K
+ * slice, at most 32 MiB), or 0 when the plain kernels run.  0 when m or n is 0; FGFP8_EINVAL (-1) when m < 0,
+ * n < 0, k is not a positive multiple of 128, or the limits of
+ * gemm_fp8_nt_bf16_splitk on n and k are exceeded.  Host only: launches
  * nothing and needs no device.
  */
 int64_t gemm_fp8_nt_bf16_splitk_workspace(int64_t m, int64_t n, int64_t k);
@@ -242,7 +254,8 @@ int64_t gemm_fp8_nt_bf16_splitk_workspace(int64_t m, int64_t n, int64_t k);
  *
  * Limit: gemm_fp8_nt_bf16_splitk_workspace(m, n, k) must not exceed
  * FGFP8_SCRATCH_BYTES (for m = 64 up to about 3600 units of 128 columns x 128
- * K, e.g. n = k = 7168), else FGFP8_ESCRATCH and nothing is written.
+ * K, e.g. n = k = 7168; for m > 64 up to 512 tile slices, which every plan
+ * keeps to), else FGFP8_ESCRATCH and nothing is written.
  * Every call on a GPU shares that GPU's array: calls that overlap on one GPU
  * (two streams, or two threads) race and give wrong results, so order them.
  * Nothing in the array has to start at any value: each call writes every

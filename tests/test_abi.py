@@ -297,10 +297,15 @@ def splitk(lib, **kw):
                                        a["st"])
 
 
+# m = 512, n = 256, k = 2048: 8 tiles of 128x128 in 2 K slices, a 1 MiB workspace
+KSLICE = dict(m=512, sald=512, k=2048, lda=2048, ldb=2048, sbld=16)
+
+
 @pytest.mark.parametrize("kw", [
-    dict(m=65, sald=65), dict(k=200), dict(k=0), dict(lda=200), dict(sbld=1), dict(ldd=252), dict(fmt=5),
+    dict(k=200), dict(k=0), dict(lda=200), dict(sbld=1), dict(ldd=252), dict(fmt=5),
     dict(A=None), dict(ws=None), dict(ws=ctypes.c_void_p(0x40008)), dict(wsb=2 * 4 * 64 * 512 - 4),
-    dict(D=ctypes.c_void_p(0x10004)), dict(m=-1),
+    dict(D=ctypes.c_void_p(0x10004)), dict(m=-1), dict(KSLICE, ws=None), dict(KSLICE, wsb=(1 << 20) - 4),
+    dict(KSLICE, sald=511), dict(KSLICE, ws=ctypes.c_void_p(0x40004)),
 ])
 def test_splitk_rejects(lib, kw):
     assert splitk(lib, **kw) == -1
@@ -313,9 +318,21 @@ def test_splitk_zero_size_is_ok(lib):
 def test_splitk_workspace_size(lib):
     ws = lib.gemm_fp8_nt_bf16_splitk_workspace
     assert ws(0, 4096, 7168) == 0 and ws(64, 0, 7168) == 0
-    for bad in [(65, 4096, 7168), (-1, 4096, 7168), (64, -1, 7168), (64, 4096, 0), (64, 4096, 100),
-                (64, 1 << 40, 128 * 1024)]:
+    for bad in [(-1, 4096, 7168), (64, -1, 7168), (64, 4096, 0), (64, 4096, 100),
+                (64, 1 << 40, 128 * 1024), (512, 4096, 100)]:
         assert ws(*bad) == -1
+    # m > 64: one 128x128 fp32 slot per tile and K slice; with at most 128 tiles, S =
+    # min(4, K blocks / 8) when that is 2 or more, else 0 (the plain kernel)
+    slot = 128 * 128 * 4
+    assert ws(512, 4096, 7168) == 128 * 4 * slot          # 32 MiB: the static scratch's size
+    assert ws(200, 1000, 2048) == 16 * 2 * slot          # 16 K blocks: two slices of 8
+    assert ws(65, 130, 3200) == 2 * 3 * slot             # 25 K blocks: three slices
+    assert ws(128, 7168, 4096) == 56 * 4 * slot
+    # beyond 256 workgroups a slice needs 12 K blocks: 96 and 112 tiles of 32 blocks take 2
+    assert ws(384, 4096, 4096) == 96 * 2 * slot and ws(256, 7168, 4096) == 112 * 2 * slot
+    for zero in [(65, 256, 256), (512, 4096, 1024), (4096, 4096, 7168), (512, 7168, 4096), (1024, 2176, 7168)]:
+        assert ws(*zero) == 0                              # too few K blocks, or more than 128 tiles
+    assert ws(1024, 2048, 7168) == 128 * 4 * slot          # 128 tiles: the most that take slices
     # two partial-sum slots per workgroup of 16*ceil(m/16) x 128 fp32 (16, 32 or 64 rows); the
     # workgroup count depends on n and k only, at least one per 8 units (128-column tile x K
     # block) and at most one per unit
@@ -340,7 +357,7 @@ def noalloc(lib, **kw):
                                                a["sb"], a["sbld"], a["D"], a["ldd"], a["m"], a["n"], a["k"], a["st"])
 
 
-@pytest.mark.parametrize("kw", [dict(m=65, sald=65), dict(k=200), dict(lda=200), dict(sbld=1), dict(ldd=7164),
+@pytest.mark.parametrize("kw", [dict(m=512, sald=511), dict(k=200), dict(lda=200), dict(sbld=1), dict(ldd=7164),
                                 dict(fmt=5), dict(A=None), dict(D=ctypes.c_void_p(0x10004)), dict(m=-1)])
 def test_splitk_noalloc_rejects(lib, kw):
     assert noalloc(lib, **kw) == -1

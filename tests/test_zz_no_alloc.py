@@ -17,7 +17,7 @@ import torch
 import fine_grained_block_token_amd as fg
 import oracle
 import synth_inputs as si
-from gpu_util import check_bf16_gemm, mfma_truncation_bound, say
+from gpu_util import check_bf16_gemm, mfma_truncation_bound, sample_idx, say
 
 pytestmark = pytest.mark.gpu
 
@@ -74,6 +74,30 @@ def test_noalloc_matches_workspace_entry_point(gpu):
         ref, absum = oracle.gemm_nt(qa, sa, qb, sb)
         check_bf16_gemm(got_na, ref, absum, mfma_truncation_bound(qa, sa, qb, sb), k // 128,
                         f"splitk noalloc {(m, n, k)}")
+
+
+def test_noalloc_kslices_matches_workspace_entry_point(gpu):
+    # m > 64 takes K slices of 128x128 tiles: 512 x 4096 x 7168 fills all 32 MiB (128
+    # tiles x 4 slices of 64 KB), then a smaller ragged problem (6 tiles x 2 slices)
+    for m, n, k in [(512, 4096, 7168), (130, 300, 2176)]:
+        wsb = fg.gemm_fp8_nt_bf16_splitk_workspace(m, n, k)
+        assert 0 < wsb <= SCRATCH_BYTES
+        qa, sa, qb, sb = _operands(m, n, k)
+        A, sa_d, B, sb_d = _device(qa, sa, qb, sb)
+        ws = torch.full((wsb // 4,), float("nan"), dtype=torch.float32, device="cuda")
+        D_ws, D_na = _out(m, n), _out(m, n)
+        say("gemm_fp8_nt_bf16_splitk", (m, n, k))
+        fg.gemm_fp8_nt_bf16_splitk(A, sa_d, B, sb_d, D_ws[:, :n].view(torch.bfloat16), ws)
+        torch.cuda.synchronize()
+        say("gemm_fp8_nt_bf16_splitk_noalloc", (m, n, k))
+        fg.gemm_fp8_nt_bf16_splitk_noalloc(A, sa_d, B, sb_d, D_na[:, :n].view(torch.bfloat16))
+        torch.cuda.synchronize()
+        got_ws, got_na = _bits(D_ws, n), _bits(D_na, n)
+        assert np.array_equal(got_na, got_ws), f"noalloc differs from the workspace entry point at {(m, n, k)}"
+        ii, jj = sample_idx(m, n, 20000, 5)
+        ref, absum = oracle.gemm_nt(qa, sa, qb, sb, idx=(ii, jj))
+        check_bf16_gemm(got_na[ii, jj], ref, absum, mfma_truncation_bound(qa, sa, qb, sb, idx=(ii, jj)), k // 128,
+                        f"splitk noalloc kslices {(m, n, k)}")
 
 
 def test_noalloc_refuses_problems_beyond_the_scratch(gpu):
