@@ -345,6 +345,22 @@ def extra_kernels(fg, torch, si):
         out[f"gemm_ue8m0_g32_{m}x{n}x{k}"] = _measure(torch, "TFLOPS", 2.0 * m * n * k,
                                                       lambda: fg.gemm_fp8_nt_bf16_ue8m0_g32(A, wa, B, wb, D))
         del a, b, A, B, wa, wb, D
+    # the casts' UE8M0 option (power-of-two 1x128 and 128x128 scales) at the same shapes: one or
+    # two rounds of 256x256 tiles, so the wide kernel runs
+    for (m, n, k) in ((4096, 7168, 7168), (8192, 4096, 7168)):
+        a = si.randn((m, k), si.SEED_A, 0.1).cuda()
+        b = si.randn((n, k), si.SEED_B, 0.1).cuda()
+        A = torch.empty((m, k), dtype=torch.uint8, device="cuda")
+        B = torch.empty((n, k), dtype=torch.uint8, device="cuda")
+        sa = fg.mn_major_scales(m, k // 128)
+        sb = torch.empty((-(-n // 128), k // 128), dtype=torch.float32, device="cuda")
+        fg.cast_per_token(a, A, sa, 128, fg.SF_UE8M0)
+        fg.cast_per_block(b, B, sb, sf_fmt=fg.SF_UE8M0)
+        D = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+        torch.cuda.synchronize()
+        out[f"gemm_ue8m0_{m}x{n}x{k}"] = _measure(torch, "TFLOPS", 2.0 * m * n * k,
+                                                  lambda: fg.gemm_fp8_nt_bf16_ue8m0(A, sa, B, sb, D, fg.SF_UE8M0))
+        del a, b, A, B, sa, sb, D
     # its weight gradient at the linear step's shape: dW [4096, 7168] += dY^T x over 8192 tokens,
     # operands cast along tokens from the transposed views
     T, I, O = si.LINEAR["tokens"], si.LINEAR["d_in"], si.LINEAR["d_out"]
@@ -511,7 +527,7 @@ def measured_traffic(op):
         entry = data["ops"][op]
     except (OSError, IndexError, KeyError, ValueError):
         return None
-    files = ["gemm.hip" if op.startswith("gemm") else "cast.hip", "device_common.h", "launch.h"]
+    files = (["gemm.hip", "tile_common.h"] if op.startswith("gemm") else ["cast.hip"]) + ["device_common.h", "launch.h"]
     return entry["traffic_bytes"] if entry["source"] == _source_digest(files) else None
 
 

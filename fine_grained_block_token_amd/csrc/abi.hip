@@ -6,6 +6,7 @@
 #include <cstring>
 
 #include "fgfp8.h"
+#include "gemm_wide.h"
 #include "launch.h"
 
 namespace {
@@ -287,6 +288,9 @@ int gemm_fp8_nt_bf16_ue8m0(const uint8_t *A, int64_t lda, const void *sa, int sa
   if (dev != FGFP8_OK) return dev;
   fgfp8::GemmArgs a{A, lda, sa, sa_fmt, sa_ld, B, ldb, sb, sb_ld, D, ldd, m, n, k, false};
   a.ue_gran = 128;
+  // one or two full rounds of 256x256 tiles: the wide kernel (same bits, fewer copied
+  // bytes per flop); otherwise the 128x128 kernel fills the part better
+  if (fgfp8::gemm_wide_fits(m, n, k)) return launched(fgfp8::launch_gemm_wide(a, static_cast<hipStream_t>(stream)));
   return launched(fgfp8::launch_gemm_g32(a, static_cast<hipStream_t>(stream)));
 }
 

@@ -321,7 +321,9 @@ int gemm_fp8_nt_bf16_ue8m0_g32(const uint8_t *A, int64_t lda, const uint32_t *sa
  * the GEMM of "DeepGEMM Essentials", Parts 1 and 6):
  *     D[i, j] = sum_kb 2^(ea(i,kb) + eb(j/128,kb)) sum_{t in kb} A[i, t] B[j, t],
  * rounded to bf16.  The exponents are applied by the scaled FP8 MFMA, which
- * accumulates across K in fp32: no per-block promotion.
+ * accumulates across K in fp32: no per-block promotion.  Products with 256 to
+ * 512 output tiles of 256x256 (and k >= 1024) run a 256x256-tile kernel, the
+ * others 128x128 tiles; both give the same result.
  *
  * sa_fmt   FGFP8_SF_UE8M0 (sa fp32 2^e, (i, kb) at sa[kb*sa_ld + i]) or
  *          FGFP8_SF_PACKED_UE8M0 (int32 words, byte kb%4 of word (i, kb/4) at

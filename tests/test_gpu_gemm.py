@@ -455,6 +455,46 @@ def test_gemm_ue8m0_closed_form_pins_scale_indexing(gpu):
     assert np.array_equal(got, oracle.bf16_bits_to_f32(oracle.round_bf16(want)).astype(np.float64))
 
 
+# One or two full rounds of 256x256 tiles (256 to 512) and 8 K blocks: the wide kernel
+# (4 waves of 128x128 on the 32x32x64 scaled MFMA).  Ragged shapes: 4100 rows leave 4
+# in the last tile row; 4000 columns leave 160 in the last tile column, across two
+# B blocks; 3900 leave 60, so the tile's second B block lies past the matrix.
+@pytest.mark.parametrize("mnk", [(4100, 4000, 1024), (4100, 3900, 1152), (4096, 4096, 1024)])
+@pytest.mark.parametrize("fmt", [fg.SF_UE8M0, fg.SF_PACKED_UE8M0], ids=["ue8m0", "packed"])
+def test_gemm_ue8m0_wide_sampled(gpu, mnk, fmt):
+    m, n, k = mnk
+    qa, sa, qb, sb = _cast_operands_ue8m0(m, n, k, fmt, scale=0.1)
+    sa_v = oracle.unpack_ue8m0(sa, k // 128) if fmt == fg.SF_PACKED_UE8M0 else sa
+    got = _run_gemm_ue8m0(qa, sa, qb, sb, fmt)
+    ii, jj = sample_idx(m, n, 20000, 13)
+    ref, absum = oracle.gemm_nt(qa, sa_v, qb, sb, idx=(ii, jj))
+    tb = mfma_truncation_bound(qa, sa_v, qb, sb, idx=(ii, jj))
+    check_bf16_gemm(got[ii, jj], ref, absum, tb, k // 8, f"gemm ue8m0 wide {mnk}")
+
+
+@pytest.mark.parametrize("fmt", [fg.SF_UE8M0, fg.SF_PACKED_UE8M0], ids=["ue8m0", "packed"])
+def test_gemm_ue8m0_wide_closed_form(gpu, fmt):
+    # all-ones operands with per-(row, K block) and per-(128-column block, K block)
+    # exponents: every output is 128 * sum_kb 2^(ea + eb), exact in fp32, so the wide
+    # kernel's rows, columns, K halves and both B blocks of a tile are pinned exactly
+    m, n, k = 4100, 3900, 1024
+    KB = k // 128
+    rng = np.random.default_rng(26)
+    ea = rng.integers(-5, 6, (m, KB))
+    eb = rng.integers(-5, 6, (-(-n // 128), KB))
+    if fmt == fg.SF_PACKED_UE8M0:
+        bytes_ = (ea + 127).astype(np.uint32)
+        sa = (bytes_.reshape(m, -1, 4) << (8 * np.arange(4, dtype=np.uint32))).sum(axis=2).astype(np.uint32)
+    else:
+        sa = np.ldexp(1.0, ea).astype(np.float32)
+    sb = np.ldexp(1.0, eb).astype(np.float32)
+    got = oracle.bf16_bits_to_f32(_run_gemm_ue8m0(np.full((m, k), 0x38, np.uint8), sa, np.full((n, k), 0x38, np.uint8),
+                                                  sb, fmt)).astype(np.float64)
+    want = 128 * (np.ldexp(1.0, ea) @ np.ldexp(1.0, eb).T)    # [m, n blocks], exact in fp64
+    want = np.repeat(want, 128, axis=1)[:, :n]
+    assert np.array_equal(got, oracle.bf16_bits_to_f32(oracle.round_bf16(want)).astype(np.float64))
+
+
 def test_gemm_ue8m0_prefill_sampled(gpu):
     m, n, k = 4096, 7168, 7168
     qa, sa, qb, sb = _cast_operands_ue8m0(m, n, k, fg.SF_PACKED_UE8M0, scale=0.1)
