@@ -273,6 +273,7 @@ int gemm_fp8_nt_bf16_ue8m0_g32(const uint8_t *A, int64_t lda, const uint32_t *sa
   if (dev != FGFP8_OK) return dev;
   fgfp8::GemmArgs a{A, lda, sa, kSfPackedUe8m0, sa_ld, B, ldb, reinterpret_cast<const float *>(sb), sb_ld,
                     D, ldd, m, n, k, false};
+  if (fgfp8::gemm_wide_fits(m, n, k)) return launched(fgfp8::launch_gemm_wide(a, static_cast<hipStream_t>(stream)));
   return launched(fgfp8::launch_gemm_g32(a, static_cast<hipStream_t>(stream)));
 }
 

@@ -59,8 +59,29 @@ __device__ __forceinline__ v8i frag32(const uint8_t *tile, int row, int h, int s
   return r;
 }
 
-template <bool PACKED>
+// Group-32 operand layout.  Measured on MI355X with one-hot K positions: the scale of
+// lane r (r < 32) applies to bytes 0-15 (v0-3) of row r in both lane groups, the scale
+// of lane r + 32 to bytes 16-31 (v4-7).  So lane (r32, h) of the block's MFMA s loads
+// 16-byte chunk 4s + h of its row into v0-3 and chunk 4s + 2 + h into v4-7: the two
+// v0-3 halves of a row form 32-K group 2s, the two v4-7 halves group 2s + 1, and lane
+// (r32, h) carries the exponent of group 2s + h.  A and B use the same K order.
+__device__ __forceinline__ v8i frag32_g32(const uint8_t *tile, int row, int h, int s) {
+  const u32x4 lo = *reinterpret_cast<const u32x4 *>(tile + swz(row, 4 * s + h));
+  const u32x4 hi = *reinterpret_cast<const u32x4 *>(tile + swz(row, 4 * s + 2 + h));
+  v8i r;
+  r[0] = (int)lo[0]; r[1] = (int)lo[1]; r[2] = (int)lo[2]; r[3] = (int)lo[3];
+  r[4] = (int)hi[0]; r[5] = (int)hi[1]; r[6] = (int)hi[2]; r[7] = (int)hi[3];
+  return r;
+}
+
+// Exponent layouts: 1x128 A exponents as fp32 2^e or packed words (byte kb % 4 of
+// word kb / 4) with one fp32 2^e per 128x128 block of B; or group 32 on both
+// operands (one word per row or column and 128-K block, byte g for 32-K group g).
+enum : int { kWideUeFloat = 0, kWideUePacked = 1, kWideG32 = 2 };
+
+template <int MODE>
 __global__ __launch_bounds__(WideCfg::kThreads, 1) void gemm_wide_kernel(GemmArgs g, int tiles_m, int tiles_n) {
+  constexpr bool G32 = MODE == kWideG32;
   using C = WideCfg;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * C::kStageBytes];
   const int t = threadIdx.x, lane = t & 63;
@@ -86,10 +107,13 @@ __global__ __launch_bounds__(WideCfg::kThreads, 1) void gemm_wide_kernel(GemmArg
     off[C::kALoads + i] = (uint32_t)(min((int64_t)row, n - 1 - n0) * g.ldb) + (uint32_t)(chunk * 16);
   }
   const uint32_t sa_off = 4u * (uint32_t)min((int64_t)(64 * wv + lane), m - 1 - m0);
-  // every wave copies one B block scale into its own slot (waves 2, 3 repeat those of
-  // waves 0, 1), so that no copy depends on a wave-dependent branch
+  // B: with 1x128 exponents every wave copies one block scale into its own slot (waves
+  // 2, 3 repeat those of waves 0, 1), so that no copy depends on a wave-dependent
+  // branch; with group 32 each wave copies the words of 64 of the tile's columns
   const int64_t sb_blk = min((int64_t)(n0 >> 7) + (wv & 1), nbl - 1);
+  const uint32_t sb_off = 4u * (uint32_t)min((int64_t)(64 * wv + lane), n - 1 - n0);
   const uint32_t *sa = reinterpret_cast<const uint32_t *>(g.sa);
+  const uint32_t *sbw = reinterpret_cast<const uint32_t *>(g.sb);
   auto copy_one = [&](int c, int kb, uint8_t *st) {
     if (c < C::kALoads)
       load_lds16(g.A + m0 * g.lda + (int64_t)kb * kBK, off[c], st + 1024 * (c * C::kWaves + wv));
@@ -98,9 +122,12 @@ __global__ __launch_bounds__(WideCfg::kThreads, 1) void gemm_wide_kernel(GemmArg
                  st + C::kABytes + 1024 * ((c - C::kALoads) * C::kWaves + wv));
   };
   auto copy_scales = [&](int kb, uint8_t *st) {
-    const int64_t col = PACKED ? (kb >> 2) : kb;
+    const int64_t col = MODE == kWideUePacked ? (kb >> 2) : kb;
     load_lds4(sa + col * g.sa_ld + m0, sa_off, st + C::kSaOff + 256 * wv);
-    load_lds4(g.sb + sb_blk * g.sb_ld + kb, 0u, st + C::kSbOff + 256 * wv);
+    if constexpr (G32)
+      load_lds4(sbw + (int64_t)kb * g.sb_ld + n0, sb_off, st + C::kSbOff + 256 * wv);
+    else
+      load_lds4(g.sb + sb_blk * g.sb_ld + kb, 0u, st + C::kSbOff + 256 * wv);
   };
 
   v16f acc[4][4];
@@ -121,17 +148,30 @@ __global__ __launch_bounds__(WideCfg::kThreads, 1) void gemm_wide_kernel(GemmArg
     const uint8_t *st = smem + (kb & 1) * C::kStageBytes;
     uint8_t *nst = smem + ((kb + 1) & 1) * C::kStageBytes;
     const int kn = min(kb + 1, KB - 1);
-    // exponent bytes: bits 30-23 of an fp32 2^e, or byte kb % 4 of a packed word
-    const int sh = PACKED ? 8 * (kb & 3) : 23;
-    int ea[4];
+    // exponent words of the lane's rows (A) and columns (B, group 32) or B's block
+    // scale; the byte is bits 30-23 of an fp32 2^e, byte kb % 4 of a packed 1x128
+    // word, or byte 2s + hh of a group-32 word (MFMA s, below)
+    uint32_t wa[4], wb[4];
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
-      ea[mi] = (int)((*reinterpret_cast<const uint32_t *>(st + C::kSaOff + 4 * (wm + 32 * mi + r32)) >> sh) & 0xFFu);
-    const int eb = (int)((*reinterpret_cast<const uint32_t *>(st + C::kSbOff + 256 * (wn >> 7)) >> 23) & 0xFFu);
+    for (int i = 0; i < 4; ++i) {
+      wa[i] = *reinterpret_cast<const uint32_t *>(st + C::kSaOff + 4 * (wm + 32 * i + r32));
+      wb[i] = G32 ? *reinterpret_cast<const uint32_t *>(st + C::kSbOff + 4 * (wn + 32 * i + r32))
+                  : *reinterpret_cast<const uint32_t *>(st + C::kSbOff + 256 * (wn >> 7));
+    }
+    // A: group-32 byte, byte kb % 4 of a packed 1x128 word, or an fp32 2^e; B: group-32
+    // byte, or its block's fp32 2^e in both 1x128 modes
+    auto ex_a = [&](uint32_t w, int s) {
+      const int sh = G32 ? 8 * (2 * s + hh) : MODE == kWideUePacked ? 8 * (kb & 3) : 23;
+      return (int)((w >> sh) & 0xFFu);
+    };
+    auto ex_b = [&](uint32_t w, int s) { return (int)((w >> (G32 ? 8 * (2 * s + hh) : 23)) & 0xFFu); };
+    auto fr = [&](const uint8_t *tile, int row, int s) {
+      return G32 ? frag32_g32(tile, row, hh, s) : frag32(tile, row, hh, s);
+    };
     v8i af[2][4], bf[2][4];
-    af[0][0] = frag32(st, wm + r32, hh, 0);
+    af[0][0] = fr(st, wm + r32, 0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) bf[0][i] = frag32(st + C::kABytes, wn + 32 * i + r32, hh, 0);
+    for (int i = 0; i < 4; ++i) bf[0][i] = fr(st + C::kABytes, wn + 32 * i + r32, 0);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
@@ -139,14 +179,14 @@ __global__ __launch_bounds__(WideCfg::kThreads, 1) void gemm_wide_kernel(GemmArg
       for (int q = 0; q < 16; ++q) {
         // snake order over the 4x4 tiles: each MFMA needs at most one new fragment
         const int mi = q >> 2, ni = (mi & 1) ? 3 - (q & 3) : (q & 3);
-        // first operand B (its block's exponent), second A (the lane's row exponent)
-        acc[mi][ni] =
-            __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[s][ni], af[s][mi], acc[mi][ni], 0, 0, 0, eb, 0, ea[mi]);
+        // first operand B (its column's or block's exponent), second A (its row's)
+        acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[s][ni], af[s][mi], acc[mi][ni], 0, 0, 0,
+                                                                      ex_b(wb[ni], s), 0, ex_a(wa[mi], s));
         if (s == 0) {
           // this half's A fragments 1-3, then the other half's fragments
-          if (q < 3) af[0][q + 1] = frag32(st, wm + 32 * (q + 1) + r32, hh, 0);
-          else if (q < 7) af[1][q - 3] = frag32(st, wm + 32 * (q - 3) + r32, hh, 1);
-          else if (q < 11) bf[1][q - 7] = frag32(st + C::kABytes, wn + 32 * (q - 7) + r32, hh, 1);
+          if (q < 3) af[0][q + 1] = fr(st, wm + 32 * (q + 1) + r32, 0);
+          else if (q < 7) af[1][q - 3] = fr(st, wm + 32 * (q - 3) + r32, 1);
+          else if (q < 11) bf[1][q - 7] = fr(st + C::kABytes, wn + 32 * (q - 7) + r32, 1);
           copy_one(q, kn, nst);   // one copy of the next block per MFMA
         } else if (q == 0) {
           copy_scales(kn, nst);
@@ -193,10 +233,12 @@ hipError_t launch_gemm_wide(const GemmArgs &a, hipStream_t st) {
   const int tiles_n = (int)((a.n + WideCfg::kBN - 1) / WideCfg::kBN);
   const int per_xcd = (tiles_m * tiles_n + kXcds - 1) / kXcds;
   const dim3 grid((unsigned)(per_xcd * kXcds));
-  if (a.sa_fmt == kSfPackedUe8m0)
-    hipLaunchKernelGGL((gemm_wide_kernel<true>), grid, dim3(WideCfg::kThreads), 0, st, a, tiles_m, tiles_n);
+  if (a.ue_gran == 32)
+    hipLaunchKernelGGL((gemm_wide_kernel<kWideG32>), grid, dim3(WideCfg::kThreads), 0, st, a, tiles_m, tiles_n);
+  else if (a.sa_fmt == kSfPackedUe8m0)
+    hipLaunchKernelGGL((gemm_wide_kernel<kWideUePacked>), grid, dim3(WideCfg::kThreads), 0, st, a, tiles_m, tiles_n);
   else
-    hipLaunchKernelGGL((gemm_wide_kernel<false>), grid, dim3(WideCfg::kThreads), 0, st, a, tiles_m, tiles_n);
+    hipLaunchKernelGGL((gemm_wide_kernel<kWideUeFloat>), grid, dim3(WideCfg::kThreads), 0, st, a, tiles_m, tiles_n);
   return hipGetLastError();
 }
 

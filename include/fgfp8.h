@@ -307,7 +307,9 @@ int gemm_fp8_nt_bf16_cast(const uint8_t *A, int64_t lda, const void *sa, int sa_
  * B    E4M3 [n, k], as A.
  * sb   int32 words, (j, kb) at sb[kb*sb_ld + j], sb_ld >= n.
  * D    bf16 [m, n] row-major, ldd >= n, multiple of 8; 16-B aligned.
- * k must be a positive multiple of 128.
+ * k must be a positive multiple of 128.  Products with 256 to 512 output tiles
+ * of 256x256 (and k >= 1024) run a 256x256-tile kernel, the others 128x128
+ * tiles; both give the same result.
  */
 int gemm_fp8_nt_bf16_ue8m0_g32(const uint8_t *A, int64_t lda, const uint32_t *sa, int64_t sa_ld,
                                const uint8_t *B, int64_t ldb, const uint32_t *sb, int64_t sb_ld,

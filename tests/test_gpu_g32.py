@@ -73,6 +73,36 @@ def test_g32_closed_form_pins_group_scales(gpu):
     assert np.array_equal(got, oracle.bf16_bits_to_f32(oracle.round_bf16(want)).astype(np.float64))
 
 
+# One or two full rounds of 256x256 tiles (256 to 512) and 8 K blocks: the wide kernel,
+# whose lane (r, h) of the block's MFMA s carries 16-byte K chunks 4s + h and 4s + 2 + h
+# under the exponent of group 2s + h.  Ragged: 4100 rows, 4000 and 3900 columns.
+@pytest.mark.parametrize("mnk", [(4100, 4000, 1024), (4100, 3900, 1152), (4096, 4096, 1024)])
+def test_g32_wide_sampled(gpu, mnk):
+    m, n, k = mnk
+    qa, wa, qb, wb = _operands(m, n, k, scale=0.1)
+    sa, sb = oracle.unpack_ue8m0(wa, k // 32), oracle.unpack_ue8m0(wb, k // 32)
+    got = _run(qa, wa, qb, wb)
+    ii, jj = sample_idx(m, n, 20000, 14)
+    ref, absum = oracle.gemm_nt_g32(qa, sa, qb, sb, idx=(ii, jj))
+    tb = mfma_truncation_bound(qa, sa, qb, sb, sb_block=False, idx=(ii, jj), group=32)
+    check_bf16_gemm(got[ii, jj], ref, absum, tb, k // 8, f"g32 wide {mnk}")
+
+
+def test_g32_wide_closed_form(gpu):
+    # all-ones operands, a distinct power of two per (row, 32-K group) and (column, group):
+    # every output is 32 * sum_g 2^(ea + eb), exact in fp32, so the lane-to-group
+    # exponent mapping of the wide kernel is pinned exactly
+    m, n, k = 4100, 3900, 1024
+    rng = np.random.default_rng(27)
+    ea = rng.integers(-4, 5, (m, k // 32))
+    eb = rng.integers(-4, 5, (n, k // 32))
+    pack = lambda e: (e + 127).astype(np.uint32).reshape(e.shape[0], -1, 4) @ (1 << (8 * np.arange(4, dtype=np.uint32)))
+    wa, wb = pack(ea).astype(np.uint32), pack(eb).astype(np.uint32)
+    got = oracle.bf16_bits_to_f32(_run(np.full((m, k), 0x38, np.uint8), wa, np.full((n, k), 0x38, np.uint8), wb))
+    want = 32 * (np.ldexp(1.0, ea) @ np.ldexp(1.0, eb).T)
+    assert np.array_equal(got.astype(np.float64), oracle.bf16_bits_to_f32(oracle.round_bf16(want)).astype(np.float64))
+
+
 def test_g32_prefill_sampled(gpu):
     m, n, k = 4096, 7168, 7168
     qa, wa, qb, wb = _operands(m, n, k, scale=0.1)
