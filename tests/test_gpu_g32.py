@@ -76,7 +76,7 @@ def test_g32_closed_form_pins_group_scales(gpu):
 # One or two full rounds of 256x256 tiles (256 to 512) and 8 K blocks: the wide kernel,
 # whose lane (r, h) of the block's MFMA s carries 16-byte K chunks 4s + h and 4s + 2 + h
 # under the exponent of group 2s + h.  Ragged: 4100 rows, 4000 and 3900 columns.
-@pytest.mark.parametrize("mnk", [(4100, 4000, 1024), (4100, 3900, 1152), (4096, 4096, 1024)])
+@pytest.mark.parametrize("mnk", [(4100, 4000, 1024), (4100, 3900, 1152), (4096, 4096, 1024), (4097, 3902, 1024)])
 def test_g32_wide_sampled(gpu, mnk):
     m, n, k = mnk
     qa, wa, qb, wb = _operands(m, n, k, scale=0.1)
@@ -101,6 +101,26 @@ def test_g32_wide_closed_form(gpu):
     got = oracle.bf16_bits_to_f32(_run(np.full((m, k), 0x38, np.uint8), wa, np.full((n, k), 0x38, np.uint8), wb))
     want = 32 * (np.ldexp(1.0, ea) @ np.ldexp(1.0, eb).T)
     assert np.array_equal(got.astype(np.float64), oracle.bf16_bits_to_f32(oracle.round_bf16(want)).astype(np.float64))
+
+
+def test_g32_wide_matches_128_tiles(gpu):
+    # the m-grouped group-32 GEMM with one expert computes the same product on the
+    # 128x128 kernel; the wide kernel must give the same bits
+    m, n, k = 4100, 3900, 1024
+    qa, wa, qb, wb = _operands(m, n, k, scale=0.1)
+    wide = _run(qa, wa, qb, wb)
+    sbw = torch.zeros((1, k // 128, -(-n // 4) * 4), dtype=torch.int32)
+    sbw[0, :, :n] = torch.from_numpy(np.ascontiguousarray(wb.T).view(np.int32))
+    sb3 = sbw.cuda().transpose(1, 2)[:, :n]          # [1, n, k/128], stride(1) == 1
+    D = torch.full((m, -(-n // 8) * 8), 0x7FC0, dtype=torch.int16, device="cuda")
+    say("m_grouped_gemm_fp8_nt_bf16_ue8m0_g32_contiguous one expert", (m, n, k))
+    fg.m_grouped_gemm_fp8_nt_bf16_ue8m0_g32_contiguous(torch.from_numpy(qa).cuda(), _dev_words(wa),
+                                                        torch.from_numpy(qb).cuda()[None], sb3,
+                                                        torch.zeros(m, dtype=torch.int32, device="cuda"),
+                                                        D[:, :n].view(torch.bfloat16))
+    torch.cuda.synchronize()
+    tiles128 = D.cpu().numpy().view(np.uint16)[:, :n]
+    assert np.array_equal(wide, tiles128)
 
 
 def test_g32_prefill_sampled(gpu):

@@ -458,8 +458,9 @@ def test_gemm_ue8m0_closed_form_pins_scale_indexing(gpu):
 # One or two full rounds of 256x256 tiles (256 to 512) and 8 K blocks: the wide kernel
 # (4 waves of 128x128 on the 32x32x64 scaled MFMA).  Ragged shapes: 4100 rows leave 4
 # in the last tile row; 4000 columns leave 160 in the last tile column, across two
-# B blocks; 3900 leave 60, so the tile's second B block lies past the matrix.
-@pytest.mark.parametrize("mnk", [(4100, 4000, 1024), (4100, 3900, 1152), (4096, 4096, 1024)])
+# B blocks; 3900 leave 60, so the tile's second B block lies past the matrix; 3902
+# ends in a 2-column store (4097 rows: one row in the last tile row).
+@pytest.mark.parametrize("mnk", [(4100, 4000, 1024), (4100, 3900, 1152), (4096, 4096, 1024), (4097, 3902, 1024)])
 @pytest.mark.parametrize("fmt", [fg.SF_UE8M0, fg.SF_PACKED_UE8M0], ids=["ue8m0", "packed"])
 def test_gemm_ue8m0_wide_sampled(gpu, mnk, fmt):
     m, n, k = mnk
