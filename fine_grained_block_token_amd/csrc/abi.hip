@@ -77,6 +77,8 @@ int cast_per_token(const void *x, int x_dtype, int64_t rows, int64_t cols, int64
   } else if (x_stride_row == 1 && x_stride_col >= rows) {
     transposed = true;
     if ((x_stride_col * es) % 16 != 0) return FGFP8_EINVAL;
+    // one workgroup per 64 rows x 128 columns, column tiles along the grid's y
+    if (cdiv(cols, 128) > FGFP8_MAX_CAST_COL_TILES || cdiv(rows, 64) > FGFP8_MAX_CAST_TILES) return FGFP8_EINVAL;
   } else {
     return FGFP8_EINVAL;
   }
@@ -146,13 +148,19 @@ int cast_per_token_dual(const void *x, int x_dtype, int64_t rows, int64_t cols, 
   const int64_t unitsT = packed ? cdiv(cdiv(rows, gran_k), 4) : cdiv(rows, gran_k);
   if (!scale_layout_ok(rows, units, sf_stride_row, sf_stride_group)) return FGFP8_EINVAL;
   if (!scale_layout_ok(cols, unitsT, sfT_stride_row, sfT_stride_group)) return FGFP8_EINVAL;
-  if (cdiv(rows, 128) * cdiv(cols, 128) > 0x7FFFFFFF) return FGFP8_EINVAL;
+  // one workgroup of 256 threads per 128x128 tile: at most 2^24 tiles in a launch
+  if (rows > FGFP8_MAX_CAST_TILES * 128 || cols > FGFP8_MAX_CAST_TILES * 128 ||
+      cdiv(rows, 128) * cdiv(cols, 128) > FGFP8_MAX_CAST_TILES)
+    return FGFP8_EINVAL;
   const int dev = check_device();
   if (dev != FGFP8_OK) return dev;
   fgfp8::CastDualArgs a{x, x_dtype, rows, cols, x_ld, gran_k, sf_fmt, q, q_ld, sf, sf_stride_row,
                         sf_stride_group, qT, qT_ld, sfT, sfT_stride_row, sfT_stride_group};
   return launched(fgfp8::launch_cast_dual(a, static_cast<hipStream_t>(stream)));
 }
+
+// Size limits of the GEMMs (FGFP8_MAX_GEMM_TILES, FGFP8_MAX_GEMM_N in fgfp8.h).
+constexpr int64_t kMaxTiles = FGFP8_MAX_GEMM_TILES, kMaxN = FGFP8_MAX_GEMM_N, kMaxMN = kMaxTiles * 128;
 
 static int check_gemm_common(const uint8_t *A, int64_t lda, const void *sa, int64_t sa_ld, const uint8_t *B,
                              int64_t ldb, const float *sb, const void *D, int64_t m, int64_t n, int64_t k) {
@@ -163,7 +171,8 @@ static int check_gemm_common(const uint8_t *A, int64_t lda, const void *sa, int6
   if (!aligned(B, 16) || ldb < k || ldb % 16 != 0) return FGFP8_EINVAL;
   if (!aligned(sa, 4) || !aligned(sb, 4) || sa_ld < m) return FGFP8_EINVAL;
   if (lda >= (int64_t)1 << 24 || ldb >= (int64_t)1 << 24) return FGFP8_EINVAL;  // 32-bit in-tile offsets
-  if (cdiv(m, 128) > 0x7FFFFFFF || cdiv(n, 128) > 0x7FFFFFFF) return FGFP8_EINVAL;
+  // grid limits: tile counts stay in 32-bit ints and every launch within 2^32 work-items
+  if (m > kMaxMN || n > kMaxN || cdiv(m, 128) * cdiv(n, 128) > kMaxTiles) return FGFP8_EINVAL;
   return 1;  // proceed
 }
 
@@ -185,8 +194,9 @@ int gemm_fp8_nt_bf16(const uint8_t *A, int64_t lda, const void *sa, int sa_fmt, 
 // up to 4 fix-up workgroups per 128-column tile; K slices (m > 64) share
 // gemm_fp8_nt_bf16's tile-count limit.
 static bool splitk_fits(int64_t m, int64_t n, int64_t k) {
-  if (m > 64) return cdiv(m, 128) <= 0x7FFFFFFF && cdiv(n, 128) <= 0x7FFFFFFF;
-  return cdiv(n, 128) * (k / 128) <= 0x7FFFFFF0 && cdiv(n, 128) <= 0x1FFFFFFF;
+  if (m > kMaxMN || n > kMaxN || cdiv(m, 128) * cdiv(n, 128) > kMaxTiles) return false;
+  if (m > 64) return true;
+  return k / 128 <= 0x7FFFFFF0 && cdiv(n, 128) * (k / 128) <= 0x7FFFFFF0;
 }
 
 int64_t gemm_fp8_nt_bf16_splitk_workspace(int64_t m, int64_t n, int64_t k) {

@@ -57,6 +57,19 @@ extern "C" {
 /* bytes of the static device scratch of gemm_fp8_nt_bf16_splitk_noalloc */
 #define FGFP8_SCRATCH_BYTES (32LL << 20)
 
+/* Size limits (beyond them a call returns FGFP8_EINVAL and launches nothing).
+ * They keep tile counts in 32-bit integers and every launch within the 2^32
+ * work-items of one grid dimension.
+ *   GEMMs (every entry point): ceil(m/128) * ceil(n/128) <= FGFP8_MAX_GEMM_TILES
+ *     and n <= FGFP8_MAX_GEMM_N.
+ *   cast_per_token_dual: ceil(rows/128) * ceil(cols/128) <= FGFP8_MAX_CAST_TILES.
+ *   cast_per_token on a transposed view: ceil(rows/64) <= FGFP8_MAX_CAST_TILES
+ *     and ceil(cols/128) <= FGFP8_MAX_CAST_COL_TILES. */
+#define FGFP8_MAX_GEMM_TILES (1LL << 22)
+#define FGFP8_MAX_GEMM_N (1LL << 24)
+#define FGFP8_MAX_CAST_TILES (1LL << 24)
+#define FGFP8_MAX_CAST_COL_TILES 65535LL
+
 #define FGFP8_IN_BF16 0
 #define FGFP8_IN_FP32 1
 
@@ -79,7 +92,8 @@ extern "C" {
  *              (the transpose of a row-major [cols, x_stride_col] matrix,
  *              as the wgrad operands are read).
  *            x must be 16-byte aligned and the non-unit stride a multiple of
- *            16 bytes.
+ *            16 bytes.  A transposed view is also held to the size limits
+ *            (FGFP8_MAX_CAST_TILES, FGFP8_MAX_CAST_COL_TILES).
  * gran_k     group size along the columns: 32 or 128.  Groups per row
  *            G = ceil(cols / gran_k); a partial last group takes its amax
  *            over its valid columns only.
@@ -155,6 +169,7 @@ int cast_per_block(const void *x, int x_dtype, int64_t rows, int64_t cols, int64
  * qT, sfT  as cast_per_token on x^T: qT [cols, rows] (16-byte aligned,
  *          qT_ld >= rows, multiple of 16); sfT (c, g) or (c, w) at
  *          sfT[c*sfT_stride_row + g*sfT_stride_group], g < ceil(rows/gran_k).
+ * ceil(rows/128) * ceil(cols/128) <= FGFP8_MAX_CAST_TILES.
  * Writes exactly those elements.  rows == 0 or cols == 0: FGFP8_OK, nothing
  * launched.
  */
@@ -185,7 +200,8 @@ int cast_per_token_dual(const void *x, int x_dtype, int64_t rows, int64_t cols, 
  * sb      fp32 [ceil(n/128), k/128] row-major: (nb, kb) at sb[nb*sb_ld + kb],
  *         sb_ld >= k/128.
  * D       bf16 [m, n] row-major, ldd >= n, multiple of 8; 16-B aligned.
- * k must be a positive multiple of 128; m, n >= 0 arbitrary.
+ * k must be a positive multiple of 128; m, n >= 0 within the GEMM size limits
+ * (FGFP8_MAX_GEMM_TILES, FGFP8_MAX_GEMM_N).
  */
 int gemm_fp8_nt_bf16(const uint8_t *A, int64_t lda, const void *sa, int sa_fmt, int64_t sa_ld,
                      const uint8_t *B, int64_t ldb, const float *sb, int64_t sb_ld,
@@ -221,9 +237,8 @@ int gemm_fp8_nt_bf16(const uint8_t *A, int64_t lda, const void *sa, int sa_fmt, 
  *                  overwritten.  May be NULL when that size is 0.  Calls that
  *                  share a workspace must be ordered (one stream, or events):
  *                  two in flight at once race.
- * Other arguments, errors and m, k, n as gemm_fp8_nt_bf16; also, for m <= 64,
- * FGFP8_EINVAL when ceil(n/128) * k/128 exceeds 2^31 - 16 or ceil(n/128)
- * exceeds 2^29 - 1.
+ * Other arguments, errors, m, k, n and size limits as gemm_fp8_nt_bf16; also,
+ * for m <= 64, FGFP8_EINVAL when ceil(n/128) * k/128 exceeds 2^31 - 16.
  */
 int gemm_fp8_nt_bf16_splitk(const uint8_t *A, int64_t lda, const void *sa, int sa_fmt, int64_t sa_ld,
                             const uint8_t *B, int64_t ldb, const float *sb, int64_t sb_ld,
@@ -237,8 +252,8 @@ int gemm_fp8_nt_bf16_splitk(const uint8_t *A, int64_t lda, const void *sa, int s
  * number of workgroups (which depends on n and k only).  m > 64:
  * ceil(m/128) * ceil(n/128) * S * 128 * 128 * 4 (one slot per tile and K
  * slice, at most 32 MiB), or 0 when the plain kernels run.  0 when m or n is 0; FGFP8_EINVAL (-1) when m < 0,
- * n < 0, k is not a positive multiple of 128, or the limits of
- * gemm_fp8_nt_bf16_splitk on n and k are exceeded.  Host only: launches
+ * n < 0, k is not a positive multiple of 128, or the size limits of
+ * gemm_fp8_nt_bf16_splitk are exceeded.  Host only: launches
  * nothing and needs no device.
  */
 int64_t gemm_fp8_nt_bf16_splitk_workspace(int64_t m, int64_t n, int64_t k);

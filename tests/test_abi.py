@@ -378,3 +378,22 @@ def test_splitk_rejects_grids_beyond_32_bits(lib):
     assert lib.gemm_fp8_nt_bf16_splitk_workspace(1, n, 128) == -1
     assert splitk(lib, m=1, sald=4, n=n, k=128, lda=128, ldb=128, sbld=1, ldd=n) == -1
     assert noalloc(lib, m=1, sald=4, n=n, k=128, lda=128, ldb=128, sbld=1, ldd=n) == -1
+
+
+def test_size_limits_are_rejected_on_the_host(lib):
+    # beyond the header's size limits every call returns FGFP8_EINVAL before any device
+    # call (tile counts stay in 32-bit ints; no launch exceeds 2^32 work-items)
+    tiles, max_n = 1 << 22, 1 << 24
+    m = 2 ** 21 + 128                       # 16385 row tiles x 256 column tiles > 2^22
+    assert gemm(lib, m=m, sald=m, n=1 << 15, ldd=1 << 15) == -1
+    assert gemm(lib, m=tiles * 128 + 1, sald=tiles * 128 + 1, n=8, ldd=8) == -1
+    assert gemm(lib, m=1, n=max_n + 8, ldd=max_n + 8) == -1
+    assert wgrad(lib, m=m, sald=m, n=1 << 15, sbld=1 << 15, ldd=1 << 15) == -1
+    assert lib.gemm_fp8_nt_bf16_splitk_workspace(1, max_n + 128, 128) == -1
+    assert lib.gemm_fp8_nt_bf16_splitk_workspace(m, 1 << 15, 1024) == -1
+    # dual cast: 65536 x 257 tiles of 128 x 128 > 2^24
+    r, c = 1 << 23, 32769
+    assert dual(lib, rows=r, cols=c, xld=32776, qld=32776, qTld=r, sfr=1, sfg=r, sfTr=1, sfTg=c) == -1
+    # per-token cast of a transposed view: 65536 column tiles of 128 along the grid's y
+    c = 1 << 23
+    assert tok(lib, rows=4, cols=c, srow=1, scol=64, qld=c, sfr=1, sfg=4) == -1
