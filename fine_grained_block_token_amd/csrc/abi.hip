@@ -283,7 +283,7 @@ int gemm_fp8_nt_bf16_ue8m0_g32(const uint8_t *A, int64_t lda, const uint32_t *sa
   if (dev != FGFP8_OK) return dev;
   fgfp8::GemmArgs a{A, lda, sa, kSfPackedUe8m0, sa_ld, B, ldb, reinterpret_cast<const float *>(sb), sb_ld,
                     D, ldd, m, n, k, false};
-  if (fgfp8::gemm_wide_fits(m, n, k)) return launched(fgfp8::launch_gemm_wide(a, static_cast<hipStream_t>(stream)));
+  if (fgfp8::gemm_wide_fits(m, n, k, lda, ldb)) return launched(fgfp8::launch_gemm_wide(a, static_cast<hipStream_t>(stream)));
   return launched(fgfp8::launch_gemm_g32(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -301,7 +301,7 @@ int gemm_fp8_nt_bf16_ue8m0(const uint8_t *A, int64_t lda, const void *sa, int sa
   a.ue_gran = 128;
   // one or two full rounds of 256x256 tiles: the wide kernel (same bits, fewer copied
   // bytes per flop); otherwise the 128x128 kernel fills the part better
-  if (fgfp8::gemm_wide_fits(m, n, k)) return launched(fgfp8::launch_gemm_wide(a, static_cast<hipStream_t>(stream)));
+  if (fgfp8::gemm_wide_fits(m, n, k, lda, ldb)) return launched(fgfp8::launch_gemm_wide(a, static_cast<hipStream_t>(stream)));
   return launched(fgfp8::launch_gemm_g32(a, static_cast<hipStream_t>(stream)));
 }
 

@@ -12,8 +12,9 @@ namespace fgfp8 {
 // True when launch_gemm_wide is the faster kernel for an m x n x k bf16 GEMM with
 // power-of-two scales (UE8M0 1x128 A scales and 128x128 B block scales, or group 32
 // on both operands): one or two full rounds of
-// 256x256 tiles on a 256-CU part (256 to 512 tiles) and at least 8 K blocks.
-bool gemm_wide_fits(int64_t m, int64_t n, int64_t k);
+// 256x256 tiles on a 256-CU part (256 to 512 tiles), at least 8 K blocks, and leading
+// dimensions of A and B below 2^23.
+bool gemm_wide_fits(int64_t m, int64_t n, int64_t k, int64_t lda, int64_t ldb);
 
 // D = (A * 2^ea)(B * 2^eb)^T, bf16.  a.ue_gran 128: a.sa_fmt kSfUe8m0 (fp32 2^e) or
 // kSfPackedUe8m0 (one word per row and four K blocks), MN-major, and a.sb fp32 2^e per

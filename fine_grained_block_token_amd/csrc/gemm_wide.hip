@@ -217,13 +217,16 @@ __global__ __launch_bounds__(WideCfg::kThreads, 1) void gemm_wide_kernel(GemmArg
 
 }  // namespace
 
-bool gemm_wide_fits(int64_t m, int64_t n, int64_t k) {
+bool gemm_wide_fits(int64_t m, int64_t n, int64_t k, int64_t lda, int64_t ldb) {
   // one or two rounds of 256x256 tiles.  Measured on MI355X against the 128x128
   // scaled-MFMA kernel, same process: 8192x4096x7168 (512 tiles) 200 vs 213 us,
   // 4096x7168x7168 (448) 177 vs 197, 4096x4096x7168 (256) 102 vs 109.  With more
   // rounds the 128x128 kernel's first-round B prefetch and second workgroup per CU
   // win where B is cold: 8192x7168x4096 (896 tiles) as dgrad in the linear step took
   // 246 us against 233 (227 vs 230 isolated).
+  // A copy's in-tile offset reaches 255 rows times the leading dimension; below 2^23 it
+  // stays under 2^31, as in the 128x128 kernels, whose results are the same
+  if (lda >= (int64_t)1 << 23 || ldb >= (int64_t)1 << 23) return false;
   const int64_t tiles = ((m + 255) / 256) * ((n + 255) / 256);
   return tiles >= 256 && tiles <= 512 && k / kBK >= 8;
 }
