@@ -1,11 +1,17 @@
-"""GEMMs at the largest leading dimension the C ABI accepts (lda, ldb = 2^24 - 16 bytes,
-the limit of the kernels' 32-bit in-tile copy offsets), against the oracle.
+"""Calls at the C ABI's size limits, against the oracle.
+
+GEMMs at the largest leading dimension the ABI accepts (lda, ldb = 2^24 - 16 bytes,
+the limit of the kernels' 32-bit in-tile copy offsets).
 
 The operands sit in the first k columns of [rows, 2^24 - 16] buffers (about 2.2 GB each), so
 the copy offsets of the last tile rows come within 1% of 2^31.  Covered: the 128x128 kernel
 (one K chain, and two for 8 K blocks on a 4-tile grid), the skinny decode kernel, the
 weight gradient, and the group-32 kernel.  Tolerances as in test_gpu_gemm and test_gpu_g32.
-Definitions: "DeepGEMM Essentials", Parts 1, 6, 12-13."""
+Definitions: "DeepGEMM Essentials", Parts 1, 6, 12-13.
+
+The per-token cast of a transposed view with the most column tiles the ABI accepts
+(65535 tiles of 128 tokens along the launch grid's y), bit for bit ("DeepGEMM
+Essentials", Part 3)."""
 import numpy as np
 import pytest
 import torch
@@ -13,7 +19,7 @@ import torch
 import fine_grained_block_token_amd as fg
 import oracle
 import synth_inputs as si
-from gpu_util import check_bf16_gemm, check_wgrad, mfma_truncation_bound, say
+from gpu_util import check_bf16_gemm, check_wgrad, gpu_cast_per_token, mfma_truncation_bound, oracle_sf_bits, say
 
 pytestmark = pytest.mark.gpu
 
@@ -86,3 +92,15 @@ def test_g32_max_leading_dimension(gpu):
     ref, absum = oracle.gemm_nt_g32(qa, sa, qb, sb)
     tb = mfma_truncation_bound(qa, sa, qb, sb, sb_block=False, group=32)
     check_bf16_gemm(got, ref, absum, tb, k // 8, "g32 max ld")
+
+
+def test_transposed_cast_most_column_tiles(gpu):
+    # x [tokens, 16 features]; its transposed view [16, tokens] is cast with 1x128 groups along
+    # the tokens, 65535 column tiles of 128: the largest grid the ABI accepts for this path
+    tokens = 65535 * 128
+    x = si.cast_workload(tokens, 16, seed=si.SEED_A)
+    q, sf, _, _, _ = gpu_cast_per_token(x, 128, oracle.SF_FP32, mn_major=True, transpose=True)
+    oq, osf = oracle.cast_per_token(si.host_array(x), 128, oracle.SF_FP32, transpose=True)
+    assert q.shape == (16, tokens)
+    assert np.array_equal(q, oq), "E4M3 bytes differ"
+    assert np.array_equal(sf, oracle_sf_bits(osf)), "scale bits differ"
