@@ -18,7 +18,8 @@ import torch
 
 from . import (SF_FP32, SF_PACKED_UE8M0, SF_UE8M0, Fgfp8Error, cast_per_block, cast_per_token,
                gemm_fp8_nt_bf16, gemm_fp8_nt_bf16_ue8m0_g32, m_grouped_gemm_fp8_nt_bf16_contiguous,
-               mn_major_scales, num_groups, wgrad_gemm_fp8_nt_fp32)
+               m_grouped_gemm_fp8_nt_bf16_ue8m0_g32_contiguous, mn_major_scales, num_groups,
+               wgrad_gemm_fp8_nt_fp32)
 
 _M_ALIGNMENT = 128
 
@@ -130,7 +131,15 @@ def wgrad_gemm_fp8_fp8_fp32_nt(lhs, rhs, out: torch.Tensor) -> None:
 def m_grouped_gemm_fp8_fp8_bf16_nt_contiguous(lhs, rhs, out: torch.Tensor, m_indices: torch.Tensor) -> None:
     """MoE forward over token-contiguous expert segments: out[i] = lhs[i] @ rhs[e]^T with
     e = m_indices[i] (int32; -1 marks a padding row, which is left unwritten).  lhs as in
-    gemm_fp8_fp8_bf16_nt; rhs = (B [E, n, k] E4M3, scales [E, ceil(n/128), k/128] float32)."""
+    gemm_fp8_fp8_bf16_nt; rhs = (B [E, n, k] E4M3, scales [E, ceil(n/128), k/128] float32).
+    As in gemm_fp8_fp8_bf16_nt, int32 RHS scales select the group-32 recipe: packed words
+    [E, n, k/128] with each expert's words MN-major (stride(1) == 1, e.g. a [E, k/128, n]
+    buffer permuted), and packed group-32 LHS scales."""
     a, sa, fmt = _lhs(lhs, "m_grouped_gemm_fp8_fp8_bf16_nt_contiguous")
     b, sb = rhs
-    m_grouped_gemm_fp8_nt_bf16_contiguous(a, sa, b, sb, m_indices, out, fmt)
+    if sb.dtype == torch.int32:
+        if sa.dtype != torch.int32:
+            raise Fgfp8Error("m_grouped_gemm_fp8_fp8_bf16_nt_contiguous: packed RHS scales need packed LHS scales")
+        m_grouped_gemm_fp8_nt_bf16_ue8m0_g32_contiguous(a, sa, b, sb, m_indices, out)
+    else:
+        m_grouped_gemm_fp8_nt_bf16_contiguous(a, sa, b, sb, m_indices, out, fmt)

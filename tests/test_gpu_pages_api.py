@@ -176,3 +176,45 @@ def test_g32_flow(gpu):
     ref, absum = oracle.gemm_nt_g32(qa, sa, qb, sb)
     tb = mfma_truncation_bound(qa, sa, qb, sb, sb_block=False, group=32)
     check_bf16_gemm(got, ref, absum, tb, k // 8, "api g32")
+
+
+def test_grouped_g32_flow(gpu):
+    # int32 RHS scales select the group-32 m-grouped kernel: the LHS cast per 1 x 32 group with
+    # packed words, each expert's weight cast the same way into an MN-major slice of an
+    # [E, k/128, n] word buffer
+    E, n, k = 4, 256, 512
+    m_idx = si.grouped_layout([100, 0, 257, 31], api.get_m_alignment_for_contiguous_layout())
+    m = m_idx.size
+    x = si.randn((m, k), si.SEED_A, 0.1)
+    Ws = [si.randn((n, k), 20 + e, 0.1) for e in range(E)]
+    say("api m-grouped g32", (m, n, k), "experts", E)
+    q, s = api.per_token_cast_to_fp8(x.cuda(), use_ue8m0=True, gran_k=32, use_packed_ue8m0=True)
+    rq = torch.empty((E, n, k), dtype=torch.float8_e4m3fn, device="cuda")
+    rs = torch.empty((E, k // 128, n), dtype=torch.int32, device="cuda").permute(0, 2, 1)
+    for e in range(E):
+        api.fused_per_token_cast_to_fp8(Ws[e].cuda(), use_ue8m0=True, gran_k=32, use_packed_ue8m0=True,
+                                        out=rq[e], out_sf=rs[e])
+    idx = torch.from_numpy(m_idx).cuda()
+    out = torch.full((m, n), 7.0, dtype=torch.bfloat16, device="cuda")
+    api.m_grouped_gemm_fp8_fp8_bf16_nt_contiguous((q, s), (rq, rs), out, idx)
+    direct = torch.full_like(out, 7.0)
+    fg.m_grouped_gemm_fp8_nt_bf16_ue8m0_g32_contiguous(q, s, rq, rs, idx, direct)
+    torch.cuda.synchronize()
+    got = _bits(out)
+    assert np.array_equal(got, _bits(direct))
+    pad = m_idx < 0
+    assert (oracle.bf16_bits_to_f32(got[pad]) == 7.0).all()
+    qa, wa = oracle.cast_per_token(si.host_array(x), 32, oracle.SF_PACKED_UE8M0)
+    casts = [oracle.cast_per_token(si.host_array(w), 32, oracle.SF_PACKED_UE8M0) for w in Ws]
+    qb = np.stack([c[0] for c in casts])
+    assert np.array_equal(rq.view(torch.uint8).cpu().numpy(), qb)
+    sa = oracle.unpack_ue8m0(wa, k // 32)
+    sb = np.stack([oracle.unpack_ue8m0(c[1], k // 32) for c in casts])
+    ref, absum = oracle.m_grouped_gemm_nt_g32(qa, sa, qb, sb, m_idx)
+    rows = ~pad
+    tb = np.zeros((m, n))
+    for e in range(E):
+        r = np.nonzero(m_idx == e)[0]
+        if r.size:
+            tb[r] = mfma_truncation_bound(qa[r], sa[r], qb[e], sb[e], sb_block=False, group=32)
+    check_bf16_gemm(got[rows], ref[rows], absum[rows], tb[rows], k // 8, "api m-grouped g32")
