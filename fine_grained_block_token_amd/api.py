@@ -19,7 +19,7 @@ import torch
 from . import (SF_FP32, SF_PACKED_UE8M0, SF_UE8M0, Fgfp8Error, cast_per_block, cast_per_token,
                gemm_fp8_nt_bf16, gemm_fp8_nt_bf16_ue8m0_g32, m_grouped_gemm_fp8_nt_bf16_contiguous,
                m_grouped_gemm_fp8_nt_bf16_ue8m0_g32_contiguous, mn_major_scales, num_groups,
-               wgrad_gemm_fp8_nt_fp32)
+               wgrad_gemm_fp8_nt_fp32, wgrad_gemm_fp8_nt_fp32_ue8m0, wgrad_gemm_fp8_nt_fp32_ue8m0_g32)
 
 _M_ALIGNMENT = 128
 
@@ -114,18 +114,38 @@ def gemm_fp8_fp8_bf16_nt(lhs, rhs, out: torch.Tensor) -> None:
         gemm_fp8_nt_bf16(a, sa, b, sb, out, fmt)
 
 
-def wgrad_gemm_fp8_fp8_fp32_nt(lhs, rhs, out: torch.Tensor) -> None:
+def wgrad_gemm_fp8_fp8_fp32_nt(lhs, rhs, out: torch.Tensor, gran_k: int | None = None) -> None:
     """out [m, n] (fp32) += lhs @ rhs^T with both operands cast per token along K (the
-    tokens): lhs = (A [m, k], scales [m, k/128] float32 MN-major), rhs = (B [n, k], scales
-    [n, k/128] float32 MN-major)."""
-    a, sa, fmt = _lhs(lhs, "wgrad_gemm_fp8_fp8_fp32_nt")
+    tokens): lhs = (A [m, k], scales), rhs = (B [n, k], scales), scales MN-major.
+
+    float32 scales [m, k/128] / [n, k/128]: the fp32-scale weight gradient.  int32 packed
+    UE8M0 words on both operands: 1 x 128 groups ([rows, ceil(k/512)] words, one exponent byte
+    per 128-token block) or 1 x 32 groups ([rows, k/128] words, four bytes per block), told
+    apart by their shape; with k = 128 the two shapes coincide and ``gran_k`` (128 or 32) must
+    name the cast."""
+    what = "wgrad_gemm_fp8_fp8_fp32_nt"
+    a, sa, fmt = _lhs(lhs, what)
     b, sb = rhs
-    if fmt != SF_FP32 or sb.dtype != torch.float32:
-        raise Fgfp8Error("wgrad_gemm_fp8_fp8_fp32_nt takes float32 scales")
     if sb.shape[0] > 1 and sb.stride(0) != 1:
-        raise Fgfp8Error("wgrad_gemm_fp8_fp8_fp32_nt: RHS scales must be MN-major; pass them through "
-                         "get_col_major_tma_aligned_tensor")
-    wgrad_gemm_fp8_nt_fp32(a, sa, b, sb, out)
+        raise Fgfp8Error(f"{what}: RHS scales must be MN-major; pass them through get_col_major_tma_aligned_tensor")
+    if sa.dtype != sb.dtype or sa.dtype not in (torch.float32, torch.int32):
+        raise Fgfp8Error(f"{what}: both operands take float32 scales, or both int32 packed UE8M0 words")
+    if sa.dtype == torch.float32:
+        wgrad_gemm_fp8_nt_fp32(a, sa, b, sb, out)
+        return
+    kb = a.shape[-1] // 128
+    units = sa.shape[1] if sa.dim() == 2 else -1
+    if gran_k is None:
+        if kb == -(-kb // 4):
+            raise Fgfp8Error(f"{what}: with k = 128 packed words of 1 x 128 and 1 x 32 groups look alike; "
+                             "pass gran_k=128 or gran_k=32")
+        gran_k = 32 if units == kb else 128
+    if gran_k == 32:
+        wgrad_gemm_fp8_nt_fp32_ue8m0_g32(a, sa, b, sb, out)
+    elif gran_k == 128:
+        wgrad_gemm_fp8_nt_fp32_ue8m0(a, sa, b, sb, out, SF_PACKED_UE8M0)
+    else:
+        raise Fgfp8Error(f"{what}: gran_k must be 128 or 32")
 
 
 def m_grouped_gemm_fp8_fp8_bf16_nt_contiguous(lhs, rhs, out: torch.Tensor, m_indices: torch.Tensor) -> None:

@@ -218,3 +218,37 @@ def test_grouped_g32_flow(gpu):
         if r.size:
             tb[r] = mfma_truncation_bound(qa[r], sa[r], qb[e], sb[e], sb_block=False, group=32)
     check_bf16_gemm(got[rows], ref[rows], absum[rows], tb[rows], k // 8, "api m-grouped g32")
+
+
+@pytest.mark.parametrize("tokens,gran,pass_gran", [(256, 128, False), (256, 32, False), (128, 128, True),
+                                                   (128, 32, True)])
+def test_wgrad_packed_words_flow(gpu, tokens, gran, pass_gran):
+    # both operands cast along the tokens with packed UE8M0 words: 1 x 128 groups run the
+    # UE8M0 1x128 weight gradient, 1 x 32 groups the group-32 one; the word shapes tell them
+    # apart, except at 128 tokens, where gran_k names the cast (feature counts whose bf16 rows
+    # are whole 16-byte units, as the transposed views need)
+    d_out, d_in = 136, 200
+    dY = si.randn((tokens, d_out), si.SEED_DY)
+    x = si.randn((tokens, d_in), si.SEED_A)
+    d0 = si.randn((d_out, d_in), 5, 0.1, torch.float32)
+    say("api wgrad packed", (tokens, d_out, d_in), "gran", gran)
+    gq, gs = api.per_token_cast_to_fp8(dY.cuda().t(), use_ue8m0=True, gran_k=gran, use_packed_ue8m0=True)
+    xq, xs = api.per_token_cast_to_fp8(x.cuda().t(), use_ue8m0=True, gran_k=gran, use_packed_ue8m0=True)
+    grad = d0.cuda()
+    api.wgrad_gemm_fp8_fp8_fp32_nt((gq, gs), (xq, xs), grad, gran_k=gran if pass_gran else None)
+    direct = d0.cuda()
+    if gran == 32:
+        fg.wgrad_gemm_fp8_nt_fp32_ue8m0_g32(gq, gs, xq, xs, direct)
+    else:
+        fg.wgrad_gemm_fp8_nt_fp32_ue8m0(gq, gs, xq, xs, direct, fg.SF_PACKED_UE8M0)
+    torch.cuda.synchronize()
+    got = grad.cpu().numpy()
+    assert np.array_equal(got, direct.cpu().numpy())
+    qa, wa = oracle.cast_per_token(si.host_array(dY), gran, oracle.SF_PACKED_UE8M0, transpose=True)
+    qb, wb = oracle.cast_per_token(si.host_array(x), gran, oracle.SF_PACKED_UE8M0, transpose=True)
+    assert np.array_equal(gq.view(torch.uint8).cpu().numpy(), qa)
+    assert np.array_equal(_sf_bits(gs), oracle_sf_bits(wa)) and np.array_equal(_sf_bits(xs), oracle_sf_bits(wb))
+    sa, sb = oracle.unpack_ue8m0(wa, tokens // gran), oracle.unpack_ue8m0(wb, tokens // gran)
+    wgrad = oracle.wgrad_nt_g32 if gran == 32 else oracle.wgrad_nt
+    ref, absum = wgrad(qa, sa, qb, sb, d0.numpy())
+    check_wgrad(got, ref, absum, tokens // 32, f"api wgrad packed {tokens} gran {gran}")

@@ -72,5 +72,21 @@ def test_wgrad_refuses_bad_scales():
     sa = api.get_col_major_tma_aligned_tensor(torch.ones(8, 2))
     with pytest.raises(Fgfp8Error, match="RHS scales"):
         api.wgrad_gemm_fp8_fp8_fp32_nt((a, sa), (b, torch.ones(16, 2)), out)
-    with pytest.raises(Fgfp8Error, match="float32"):
-        api.wgrad_gemm_fp8_fp8_fp32_nt((a, sa.to(torch.int32)), (b, torch.ones(16, 2)), out)
+    sb = api.get_col_major_tma_aligned_tensor(torch.ones(16, 2))
+    with pytest.raises(Fgfp8Error, match="both operands"):
+        api.wgrad_gemm_fp8_fp8_fp32_nt((a, sa.to(torch.int32)), (b, sb), out)
+    with pytest.raises(Fgfp8Error, match="both operands"):
+        api.wgrad_gemm_fp8_fp8_fp32_nt((a, sa.to(torch.float64)), (b, sb.to(torch.float64)), out)
+
+
+def test_wgrad_packed_words_need_gran_k_when_k_is_128():
+    # with k = 128 a 1 x 128 packed word and a group-32 word are both one word per row
+    a = torch.zeros(8, 128, dtype=torch.uint8)
+    b = torch.zeros(16, 128, dtype=torch.uint8)
+    out = torch.zeros(8, 16)
+    sa = api.get_col_major_tma_aligned_tensor(torch.zeros(8, 1, dtype=torch.int32))
+    sb = api.get_col_major_tma_aligned_tensor(torch.zeros(16, 1, dtype=torch.int32))
+    with pytest.raises(Fgfp8Error, match="gran_k"):
+        api.wgrad_gemm_fp8_fp8_fp32_nt((a, sa), (b, sb), out)
+    with pytest.raises(Fgfp8Error, match="gran_k must be"):
+        api.wgrad_gemm_fp8_fp8_fp32_nt((a, sa), (b, sb), out, gran_k=64)
