@@ -258,3 +258,10 @@ def test_grouped_g32_full_compare(gpu, tokens, n, k):
         if rows.size:
             tb[rows] = mfma_truncation_bound(qa[valid[rows]], sa[valid[rows]], qb[e], sb[e], sb_block=False, group=32)
     check_bf16_gemm(got[valid], ref[valid], absum[valid], tb, k // 8, f"grouped g32 {tokens}")
+
+
+def test_grouped_g32_all_padding_writes_nothing(gpu):
+    m_idx = np.full(256, -1, np.int32)
+    qa, wa, qb, wb = _grouped_operands(m_idx, 3, 256, 384, seed=13)
+    got = _run_grouped(qa, wa, qb, wb, m_idx)
+    assert (got == 0x7FC0).all()

@@ -122,3 +122,11 @@ def test_invalid_ids_and_mixed_blocks_leave_rows_unwritten(gpu):
     rows = np.r_[0:100, 300:310]
     ref, absum = oracle.m_grouped_gemm_nt(qa[rows], sa[rows], qb, sb, m_idx[rows])
     check_bf16_gemm(got[rows], ref, absum, _trunc_bound(qa[rows], sa[rows], qb, sb, m_idx[rows]), 2, "mixed")
+
+
+def test_all_padding_writes_nothing(gpu):
+    # every row padding (-1): the launch runs and no output row is written
+    m_idx = np.full(256, -1, np.int32)
+    qa, sa, qb, sb = _operands(m_idx, 3, 256, 384, seed=12)
+    got = _run(qa, sa, qb, sb, m_idx)
+    assert (got == 0x7FC0).all()
