@@ -64,6 +64,18 @@ def test_per_token_matrix(gpu, shape, dtype, gran, fmt):
     _check_tok(x, gran, fmt, mn_major=True)
 
 
+@pytest.mark.parametrize("cols", [1, 7, 33, 129])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+@pytest.mark.parametrize("gran", [32, 128])
+@pytest.mark.parametrize("fmt", FMTS, ids=["fp32", "ue8m0", "packed"])
+def test_per_token_single_row_tiny(gpu, cols, dtype, gran, fmt):
+    # one token of 1..129 features: a lone partial group, or (129) an all-zero full group and a
+    # partial one scaled by 1e4
+    x = si.cast_workload(1, cols, seed=si.SEED_A + cols, dtype=dtype, special=cols > 128)
+    _check_tok(x, gran, fmt, mn_major=False)
+    _check_tok(x, gran, fmt, mn_major=True)
+
+
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
 @pytest.mark.parametrize("gran", [32, 128])
 @pytest.mark.parametrize("fmt", FMTS, ids=["fp32", "ue8m0", "packed"])
