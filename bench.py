@@ -497,14 +497,22 @@ def cpu_baseline(si, target_s=20.0):
 
 
 def _cpu_model():
+    """The host CPU as /proc/cpuinfo names it, with its family and model numbers (a
+    virtualised host may report only a generic name)."""
+    info = {}
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                if not line.strip():
+                    break                      # the first processor's block is enough
+                key, _, val = line.partition(":")
+                info.setdefault(key.strip(), val.strip())
     except OSError:
-        pass
-    return "unknown"
+        return "unknown"
+    name = info.get("model name", "unknown")
+    if "cpu family" in info and "model" in info:
+        name += f" (family {info['cpu family']}, model {info['model']})"
+    return name
 
 
 def _source_digest(files):
