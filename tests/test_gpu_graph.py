@@ -121,3 +121,78 @@ def test_graph_replays_match_eager(gpu):
         # wgrad accumulates into dW: zeroed, then one pass, on both sides
         assert torch.equal(got_dw, ref_dw), f"replay {r}: wgrad differs"
         del junk
+
+
+def test_graph_replays_match_eager_splitk_and_wide(gpu):
+    # split-K (stream-K shares at m = 1 and 64, K slices at m = 384), its allocation-free form,
+    # and the 256x256 kernel of the power-of-two recipes (4096 x 4096 outputs, 8 K blocks)
+    u8, f32 = torch.uint8, torch.float32
+    n, k = 1024, 2048
+    W = si.randn((n, k), si.SEED_B).cuda()
+    Wq, sW = torch.empty((n, k), dtype=u8, device="cuda"), torch.empty((n // 128, k // 128), dtype=f32, device="cuda")
+    fg.cast_per_block(W, Wq, sW, sf_fmt=fg.SF_FP32)
+    cases = []
+    for m in (1, 64, 384):
+        x = si.randn((m, k), si.SEED_A + m).cuda()
+        xq, sx = torch.empty((m, k), dtype=u8, device="cuda"), fg.mn_major_scales(m, k // 128)
+        fg.cast_per_token(x, xq, sx, 128, fg.SF_FP32)
+        wsb = fg.gemm_fp8_nt_bf16_splitk_workspace(m, n, k)
+        assert wsb > 0, (m, n, k)
+        ws = torch.empty((wsb // 4,), dtype=f32, device="cuda")
+        cases.append((xq, sx, ws, torch.empty((m, n), dtype=torch.bfloat16, device="cuda"),
+                      torch.empty((m, n), dtype=torch.bfloat16, device="cuda")))
+    M = N = 4096
+    K = 1024
+    a = si.randn((M, K), si.SEED_A, 0.1).cuda()
+    b = si.randn((N, K), si.SEED_B, 0.1).cuda()
+    A, B = torch.empty((M, K), dtype=u8, device="cuda"), torch.empty((N, K), dtype=u8, device="cuda")
+    sa, sb = fg.mn_major_scales(M, K // 128), torch.empty((N // 128, K // 128), dtype=f32, device="cuda")
+    fg.cast_per_token(a, A, sa, 128, fg.SF_UE8M0)
+    fg.cast_per_block(b, B, sb, sf_fmt=fg.SF_UE8M0)
+    A32, B32 = torch.empty((M, K), dtype=u8, device="cuda"), torch.empty((N, K), dtype=u8, device="cuda")
+    wa, wb = fg.mn_major_scales(M, K // 128, torch.int32), fg.mn_major_scales(N, K // 128, torch.int32)
+    fg.cast_per_token(a, A32, wa, 32, fg.SF_PACKED_UE8M0)
+    fg.cast_per_token(b, B32, wb, 32, fg.SF_PACKED_UE8M0)
+    yw = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    yw32 = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    torch.cuda.synchronize()
+
+    def step():
+        for xq, sx, ws, y, y_na in cases:
+            fg.gemm_fp8_nt_bf16_splitk(xq, sx, Wq, sW, y, ws)
+            fg.gemm_fp8_nt_bf16_splitk_noalloc(xq, sx, Wq, sW, y_na)
+        fg.gemm_fp8_nt_bf16_ue8m0(A, sa, B, sb, yw)
+        fg.gemm_fp8_nt_bf16_ue8m0_g32(A32, wa, B32, wb, yw32)
+
+    outs = [c[3] for c in cases] + [c[4] for c in cases] + [yw, yw32]
+
+    def clear():
+        for o in outs:
+            o.zero_()
+
+    say("graph (split-K, wide): eager reference")
+    clear()
+    step()
+    torch.cuda.synchronize()
+    ref = [o.cpu().clone() for o in outs]
+    for c in cases:                       # the allocation-free form gives the same bits
+        assert torch.equal(c[3], c[4])
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for r in range(3):
+        say("graph (split-K, wide): replay", r)
+        clear()
+        torch.cuda.synchronize()
+        junk = torch.randn(1 << 20, device="cuda").sum()
+        g.replay()
+        torch.cuda.synchronize()
+        for o, want in zip(outs, ref):
+            assert torch.equal(o.cpu(), want), f"replay {r} differs from the eager result"
+        del junk
